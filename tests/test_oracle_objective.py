@@ -1,0 +1,198 @@
+"""Pins of the oracle's objective (GRPO clipped ratio + k3 KL, GSPO) and its
+per-token coefficient, against hand-derived values, closed forms, special cases
+and finite differences."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def test_clip_truth_table():
+    """Each (ratio, advantage) case worked by hand for eps_low=0.2, eps_high=0.28:
+    the PPO min picks the clipped term only when the ratio is past the bound on
+    the side the advantage favours, and that branch has zero gradient."""
+    r = np.array([1.5, 1.5, 0.5, 0.5, 1.1, 1.0])
+    a = np.array([1.0, -2.0, 1.0, -1.0, 0.5, -1.0], np.float32)
+    old = np.full(6, -1.0)
+    logp = np.log(r) + old
+    sid = np.arange(6)
+    act = np.ones(6, bool)
+    out = oracle.grpo_objective(logp, old, None, a, sid, act, 6, 0.2, 0.28, 0.0, "token_mean")
+    pol = np.array([-1.28, 3.0, -0.5, 0.8, -0.55, 1.0])
+    dpol = np.array([0.0, 3.0, -0.5, 0.0, -0.55, 1.0])
+    assert out["policy_loss"] == pytest.approx(pol.mean(), rel=1e-14)
+    assert out["loss"] == pytest.approx(pol.mean(), rel=1e-14)
+    np.testing.assert_allclose(out["coef"], dpol / 6, rtol=1e-13, atol=1e-15)
+    assert out["kl"] == 0.0
+
+
+@pytest.mark.parametrize("delta", [0.3, -0.7])
+def test_k3_closed_form(delta):
+    """ref - logp = delta on every token: kl = e^delta - delta - 1 and the KL part
+    of the coefficient is beta * w * (1 - e^delta)."""
+    n = 5
+    logp = -np.linspace(1, 3, n)
+    ref = logp + delta
+    adv = np.zeros(1, np.float32)
+    out = oracle.grpo_objective(logp, logp, ref, adv, np.zeros(n, int), np.ones(n, bool), 1,
+                                0.2, 0.2, 0.25, "token_mean")
+    k = math.exp(delta) - delta - 1
+    assert out["kl"] == pytest.approx(k, rel=1e-13)
+    assert out["policy_loss"] == 0.0
+    assert out["loss"] == pytest.approx(0.25 * k, rel=1e-13)
+    np.testing.assert_allclose(out["coef"], 0.25 / n * (1 - math.exp(delta)), rtol=1e-13)
+
+
+def _batch(lens, masked, seed=0):
+    g = np.random.default_rng(seed)
+    sid = np.repeat(np.arange(len(lens)), lens)
+    n = len(sid)
+    act = np.ones(n, bool)
+    act[masked] = False
+    adv = g.standard_normal(len(lens)).astype(np.float32)
+    logp = -g.random(n) * 5
+    return sid, act, adv, logp
+
+
+def test_ratio_one_closed_forms():
+    """old = ref = logp: r = 1, kl = 0, and loss = -(mean advantage) — over active
+    tokens for token-mean, over live sequences for sequence-mean.  Sequence 2 is
+    fully masked and must drop out of the sequence count."""
+    lens = [3, 5, 2, 6]
+    masked = [0, 4, 8, 9, 10]         # seq 2 = tokens 8, 9 fully masked
+    sid, act, adv, logp = _batch(lens, masked)
+    a64 = adv.astype(np.float64)
+    tm = oracle.grpo_objective(logp, logp, logp, adv, sid, act, 4, .2, .2, .1, "token_mean")
+    assert tm["kl"] == 0.0
+    assert tm["loss"] == pytest.approx(-a64[sid[act]].mean(), rel=1e-13)
+    sm = oracle.grpo_objective(logp, logp, logp, adv, sid, act, 4, .2, .2, .1, "sequence_mean")
+    assert sm["loss"] == pytest.approx(-a64[[0, 1, 3]].mean(), rel=1e-13)
+    assert list(sm["counts"]) == [2, 4, 0, 5]
+    # coefficient at r = 1: -a_t w_t; inactive tokens 0
+    w = np.where(act, 1.0 / (sm["counts"][sid].clip(1) * 3), 0)
+    np.testing.assert_allclose(sm["coef"], -a64[sid] * w, rtol=1e-13)
+    assert np.all(tm["coef"][~act] == 0)
+
+
+def test_zero_advantage_zero_beta():
+    sid, act, adv, logp = _batch([4, 4], [1])
+    out = oracle.grpo_objective(logp, logp + 0.1, None, adv * 0, sid, act, 2, .2, .2, 0.0,
+                                "sequence_mean")
+    assert out["loss"] == 0.0 and np.all(out["coef"] == 0)
+
+
+def test_empty_batch_is_all_zero():
+    sid, act, adv, logp = _batch([3, 2], [0, 1, 2, 3, 4])
+    for red in ("token_mean", "sequence_mean"):
+        out = oracle.grpo_objective(logp, logp, logp, adv, sid, act, 2, .2, .2, .1, red)
+        assert (out["loss"], out["policy_loss"], out["kl"]) == (0.0, 0.0, 0.0)
+        assert np.all(out["coef"] == 0) and np.all(out["counts"] == 0)
+    out = oracle.gspo_objective(logp, logp, logp, adv, sid, act, 2, .2, .2, .1)
+    assert (out["loss"], out["policy_loss"], out["kl"]) == (0.0, 0.0, 0.0)
+    assert np.all(out["coef"] == 0)
+
+
+def test_gspo_single_token_segments_equal_grpo_sequence_mean():
+    """With one-token segments the segment ratio is the token ratio and every
+    segment weighs 1/S_live: GSPO reduces to token GRPO with sequence-mean."""
+    g = np.random.default_rng(3)
+    n = 9
+    sid = np.arange(n)
+    act = np.ones(n, bool)
+    act[4] = False
+    adv = g.standard_normal(n).astype(np.float32)
+    logp = -g.random(n) * 3
+    old = logp + g.standard_normal(n) * 0.3
+    ref = logp + g.standard_normal(n) * 0.2
+    a = oracle.gspo_objective(logp, old, ref, adv, sid, act, n, .2, .28, .05)
+    b = oracle.grpo_objective(logp, old, ref, adv, sid, act, n, .2, .28, .05, "sequence_mean")
+    for k in ("loss", "policy_loss", "kl"):
+        assert a[k] == pytest.approx(b[k], rel=1e-13)
+    np.testing.assert_allclose(a["coef"], b["coef"], rtol=1e-12, atol=1e-15)
+
+
+def test_gspo_constant_log_ratio_closed_form():
+    """A segment whose tokens all have log-ratio rho has sigma = e^rho; worked by
+    hand for three segments and eps = (3e-4, 4e-4)."""
+    lens = [4, 3, 5]
+    sid = np.repeat(np.arange(3), lens)
+    act = np.ones(12, bool)
+    act[5] = False                            # segment 1 keeps 2 active tokens
+    rho = np.array([2e-4, 1e-3, -2e-3])
+    adv = np.array([1.0, 0.5, -1.5], np.float32)
+    logp = -np.arange(12) * 0.1
+    old = logp - rho[sid]
+    out = oracle.gspo_objective(logp, old, None, adv, sid, act, 3, 3e-4, 4e-4, 0.0)
+    sig = np.exp(rho)
+    # seg 0: inside the range -> -sigma*A ; seg 1: above 1+4e-4 with A>0 -> clipped
+    # -(1+4e-4)*A ; seg 2: below 1-3e-4 with A<0 -> clipped -(1-3e-4)*A
+    pol = np.array([-sig[0] * 1.0, -(1 + 4e-4) * 0.5, -(1 - 3e-4) * -1.5])
+    assert out["policy_loss"] == pytest.approx(pol.mean(), rel=1e-13)
+    np.testing.assert_allclose(out["sigma"], sig, rtol=1e-14)
+    exp_coef = np.zeros(12)
+    exp_coef[:4] = -1.0 * sig[0] / (3 * 4)    # only segment 0 is unclipped
+    np.testing.assert_allclose(out["coef"], exp_coef, rtol=1e-13, atol=1e-18)
+    assert list(out["counts"]) == [4, 2, 5]
+    np.testing.assert_allclose(out["seg_mean_logp"][1], (logp[4] + logp[6]) / 2, rtol=1e-14)
+
+
+def test_counts_are_exact_integers():
+    g = np.random.default_rng(7)
+    sid = np.sort(g.integers(0, 40, 3000))
+    act = g.random(3000) > 0.3
+    L = oracle.sequence_counts(sid, act, 45)
+    assert L.dtype.kind == "i"
+    np.testing.assert_array_equal(L, np.bincount(sid[act], minlength=45))
+
+
+def _fd(f, x, h):
+    x0 = x.copy()
+    xp, xm = x0.copy(), x0.copy()
+    xp += h
+    xm -= h
+    return (f(xp) - f(xm)) / (2 * h)
+
+
+@pytest.mark.parametrize("level,reduction,beta", [("token", "token_mean", 0.04),
+                                                   ("token", "sequence_mean", 0.1),
+                                                   ("sequence_gspo", "sequence_mean", 0.07)])
+def test_coef_is_the_logp_derivative(level, reduction, beta):
+    """Central differences of the loss in each logp_t equal coef_t (no ratio lies
+    within 0.01 of a clip boundary, so the loss is smooth at every point)."""
+    g = np.random.default_rng(11)
+    lens = [5, 1, 6, 4]
+    sid = np.repeat(np.arange(4), lens)
+    n = len(sid)
+    act = np.ones(n, bool)
+    act[[2, 7]] = False
+    adv = g.standard_normal(4).astype(np.float32)
+    logp0 = -g.random(n) * 4
+    eps = (0.2, 0.28) if level == "token" else (0.05, 0.06)
+    noise = g.choice([-0.5, -0.1, 0.03, 0.15, 0.6], n) + g.standard_normal(n) * 0.002
+    if level != "token":
+        # segment log-ratios -0.2, 0.01, 0.3, -0.02 plus zero-mean token jitter
+        noise = np.array([0.2, -0.01, -0.3, 0.02])[sid] + np.tile([0.01, -0.01], n // 2)
+    old = logp0 + noise
+    ref = logp0 + g.standard_normal(n) * 0.2
+
+    def run(lp):
+        if level == "token":
+            return oracle.grpo_objective(lp, old, ref, adv, sid, act, 4, *eps, beta, reduction)
+        return oracle.gspo_objective(lp, old, ref, adv, sid, act, 4, *eps, beta)
+
+    out = run(logp0)
+    if level == "token":
+        assert 0 < np.sum(out["unclipped"] & act) < act.sum()
+    else:
+        assert 0 < out["unclipped"].sum() < 4
+    for t in range(n):
+        def f(v, t=t):
+            lp = logp0.copy()
+            lp[t] = v[0]
+            return run(lp)["loss"]
+        d = _fd(f, np.array([logp0[t]]), 1e-6)
+        assert d == pytest.approx(out["coef"][t], rel=1e-6, abs=1e-10), t
