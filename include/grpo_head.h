@@ -1,0 +1,213 @@
+/*
+ * grpo_head.h - C ABI of the fused LM-head GRPO / GSPO loss for MI355X (gfx950).
+ *
+ * What it computes.  For hidden states H [N, D] and an LM-head weight W [V_r, D]
+ * (nn.Linear layout, rows >= V are vocabulary padding), z = H W^T / tau over the
+ * real vocabulary [0, V).  The forward returns each token's selected log-prob
+ * log p(y_t) = z[t, y_t] - LSE_v z[t, :] without ever storing the [N, V] logits:
+ * vocabulary tiles are streamed, each tile leaves a per-token (max, sumexp)
+ * partial, and the partials are folded in ascending tile order from the identity
+ * (-inf, 0).  It then applies the clipped-ratio objective and reduces it to
+ * (loss, policy_loss, kl), and writes the per-token coefficient d loss / d logp_t.
+ * The backward recomputes each logit tile, forms
+ * dlogits = grad_output * coef_t * (onehot(y_t) - softmax) / tau, and contracts it
+ * into dH = dlogits W and dW = dlogits^T H.
+ *
+ * Sources (page title, section):
+ *   - streaming over the vocabulary so only selected-token log-probs are computed,
+ *     behind a fused-linear API (hidden states and head weight in, loss out):
+ *     Liger-Kernel PR #1160 "[GRPO] add chunked grpo streaming over vocab", Summary.
+ *   - padded versus real vocabulary; padded columns masked to -inf before the
+ *     per-tile partials; fp32 (max, sumexp) merge in a fixed global tile order and
+ *     the (-inf, 0) identity; an explicit active mask or ignore_index, inactive
+ *     targets that need not hold ignore_index; fp32 log-prob and LSE outputs:
+ *     RL-Kernel PR #291 "Add deterministic DP-aware GRPO loss on the TP-aware
+ *     logprob path", commit notes (ShardingSpec, MaskSpec / MaskMode, ReductionSpec,
+ *     LogprobOutputSpec).
+ *   - the objective is elementwise per token / per sequence; token normalisers
+ *     global_active_tokens (masked mean) and per_sequence_then_mean; the
+ *     (loss, policy_loss, kl) result; a validation flag that costs a device sync;
+ *     no division by zero for a batch with no active token; fail loudly, never a
+ *     silent fallback: same page, Overview / Key Changes, commit notes and the
+ *     review threads on validation syncs and the zero-active-token guard.
+ *   - GSPO: per-token contributions aggregated per segment (index_add), then the
+ *     loss, the new_logprobs metric and the unscaled per-token backward
+ *     coefficient, with the divisor and grad_output supplied at run time:
+ *     Fast-LLM PR #554 "Fuse the GSPO segment seam into compiled blocks", What.
+ *   The clipped surrogate is the PPO form (Schulman et al. 2017, eq. 7) with
+ *   separate bounds 1 - eps_low and 1 + eps_high; the KL term is the k3 estimator
+ *   exp(q - l) - (q - l) - 1 with l = logp, q = ref_logp; the GSPO ratio is
+ *   exp of the segment's mean log-ratio (Zheng et al. 2025, eq. 7).
+ *
+ * Conventions for every entry point.
+ *   - Pointers named as buffers are DEVICE pointers on the current HIP device,
+ *     except `p` (a host pointer to the parameter block).  The caller owns every
+ *     buffer; the library never allocates or frees device memory, keeps no state
+ *     between calls and enqueues all work on `stream` (a hipStream_t; NULL is the
+ *     null stream).  Calls return as soon as the work is enqueued, unless
+ *     p->validate is set.
+ *   - Arguments are checked on the host before anything is enqueued; a rejected
+ *     call enqueues nothing.  The return value is a grpo_head_status; on a
+ *     non-zero status grpo_head_last_error() describes it.
+ *   - Results are bitwise identical from run to run for identical inputs: every
+ *     reduction has a fixed order and no result depends on atomics.
+ *   - Calls that share a workspace must not overlap in time.
+ *
+ * Layouts.  Row-major, no padding between rows.
+ *   H [n_tokens][d_model] and W [v_rows][d_model]: bf16 or fp32 (p->dtype).
+ *   y [n_tokens] int64 target ids; mask [n_tokens] uint8 (0 = inactive) or NULL;
+ *   sid [n_tokens] int32 sequence / segment id, non-decreasing, in [0, n_seqs);
+ *   adv [n_seqs] fp32 advantage per sequence / segment;
+ *   old_logp, ref_logp, logp, lse, coef [n_tokens] fp32; counts [n_seqs] int32;
+ *   out3 [3] fp32 = {loss, policy_loss, kl}; dH [n_tokens][d_model] fp32;
+ *   dW [v_rows][d_model] fp32.
+ */
+#ifndef GRPO_HEAD_H
+#define GRPO_HEAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum grpo_head_status {
+  GRPO_HEAD_OK = 0,
+  GRPO_HEAD_INVALID_ARGUMENT = 1,   /* null pointer, bad size, bad enum or scalar */
+  GRPO_HEAD_WORKSPACE_TOO_SMALL = 2,/* ws_bytes < the matching *_workspace_size() */
+  GRPO_HEAD_NO_ACTIVE_TOKENS = 3,   /* validate only: no token is active */
+  GRPO_HEAD_TARGET_OUT_OF_RANGE = 4,/* validate only: an active target outside
+                                       [0, v_real), or sid decreasing / outside
+                                       [0, n_seqs) */
+  GRPO_HEAD_NONFINITE = 5,          /* validate only: a non-finite lse, logp, input
+                                       log-prob or loss */
+  GRPO_HEAD_HIP_ERROR = 6           /* a HIP runtime call or launch failed */
+} grpo_head_status;
+
+enum { GRPO_HEAD_BF16 = 0, GRPO_HEAD_F32 = 1 };                  /* p->dtype */
+enum { GRPO_HEAD_TOKEN_MEAN = 0, GRPO_HEAD_SEQUENCE_MEAN = 1 };  /* p->reduction */
+enum { GRPO_HEAD_LEVEL_TOKEN = 0, GRPO_HEAD_LEVEL_SEQUENCE_GSPO = 1 }; /* p->level */
+
+/* Parameter block, passed by host pointer.
+ *   n_tokens     N >= 0.  N = 0 is an empty batch: outputs are written as zeros.
+ *   d_model      D > 0, a multiple of 64.
+ *   v_real       V >= 1: the real vocabulary; columns [V, v_rows) are padding and
+ *                W rows there are never read (they may hold NaN).
+ *   v_rows       V_r >= V: rows of W and dW.
+ *   n_seqs       S >= 1 (S >= 0 when N = 0): sequences (token level) or packed
+ *                segments (GSPO).
+ *   ignore_index used only when mask is NULL: token t is active iff
+ *                y[t] != ignore_index.  With a mask the mask alone decides and an
+ *                inactive token's target is never read.
+ *   chunk_tokens backward token-chunk size (rounded up to a multiple of 256);
+ *                0 = all tokens in one chunk.  Sets the backward workspace size.
+ *   dtype        GRPO_HEAD_BF16 or GRPO_HEAD_F32 (element type of H and W; the
+ *                fp32 path keeps its dlogits in fp32, the bf16 path rounds them to
+ *                bf16, nearest-even, before the two gradient products).
+ *   reduction    token mean over active tokens, or mean over sequences (that have
+ *                an active token) of each sequence's token mean.  GSPO always
+ *                uses the sequence mean.
+ *   level        token-level ratio (GRPO) or segment-level ratio (GSPO).
+ *   validate     0: never synchronise.  1: synchronise `stream` once at the end of
+ *                the call and check the conditions of statuses 3-5.
+ *   inv_tau      1/temperature > 0, applied to the fp32 logit accumulator.
+ *   eps_low, eps_high  clip bounds >= 0 (eps_low < 1): ratio clipped to
+ *                [1 - eps_low, 1 + eps_high].
+ *   beta         KL weight >= 0.  beta > 0 needs ref_logp.
+ */
+typedef struct grpo_head_params {
+  int64_t n_tokens;
+  int64_t d_model;
+  int64_t v_real;
+  int64_t v_rows;
+  int64_t n_seqs;
+  int64_t ignore_index;
+  int64_t chunk_tokens;
+  int32_t dtype;
+  int32_t reduction;
+  int32_t level;
+  int32_t validate;
+  float inv_tau;
+  float eps_low;
+  float eps_high;
+  float beta;
+} grpo_head_params;
+
+/* Bytes of device workspace grpo_head_fwd needs (per-tile partials, target
+ * logits, per-sequence totals).  0 if p is invalid. */
+size_t grpo_head_fwd_workspace_size(const grpo_head_params* p);
+
+/* Bytes of device workspace grpo_head_bwd needs (the bf16 or fp32 dlogits of one
+ * token chunk, its transpose, and transposed copies of W and of the chunk's H);
+ * also at least grpo_head_fwd_workspace_size(p), so one buffer serves all calls.
+ * 0 if p is invalid. */
+size_t grpo_head_workspace_size(const grpo_head_params* p);
+
+/* Forward: selected log-prob, LSE, objective and per-token coefficient.
+ *   logp[t] = z[t, y_t] - lse[t] for active tokens, 0 for inactive ones;
+ *   lse[t]  = LSE over the real vocabulary, for every token;
+ *   out3    = {loss, policy_loss, kl}; loss = policy_loss + beta * kl;
+ *   coef[t] = d loss / d logp_t (0 for inactive tokens);
+ *   counts[s] = number of active tokens of sequence s.
+ * ref_logp may be NULL iff beta == 0 (kl is then 0).  old_logp and ref_logp are
+ * read for active tokens only.  With level == GSPO the objective stage is the one
+ * gspo_segment_reduce runs.
+ * Status 0, 1, 2, 6; with validate also 3, 4, 5 (outputs are then still written,
+ * but may be meaningless).  With validate == 0 an active target outside
+ * [0, v_real) gives logp = NaN for that token, and an invalid sid is clamped into
+ * [0, n_seqs); neither is reported. */
+int grpo_head_fwd(const grpo_head_params* p, const void* H, const void* W, const int64_t* y,
+                  const uint8_t* mask, const int32_t* sid, const float* adv,
+                  const float* old_logp, const float* ref_logp, float* logp, float* lse,
+                  float* out3, float* coef, int32_t* counts, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* Backward from the forward's lse and coef.
+ *   dH[t, :] = sum_v G[t, v] W[v, :],  dW[v, :] = sum_t G[t, v] H[t, :] for v < V,
+ *   dW[v, :] = 0 for V <= v < v_rows, with
+ *   G[t, v] = grad_output * coef[t] * (1[v == y_t] - exp(z[t, v] - lse[t])) * inv_tau
+ *   and G[t, :] = 0 for inactive tokens.
+ * grad_output is a DEVICE pointer to one fp32 scalar, or NULL for 1.0.
+ * dH and dW are overwritten.  Token chunks are processed in ascending order and
+ * dW accumulates them in that order.
+ * Status 0, 1, 2, 6; with validate also 4 (active target out of range) and 5
+ * (non-finite lse or coef). */
+int grpo_head_bwd(const grpo_head_params* p, const void* H, const void* W, const int64_t* y,
+                  const uint8_t* mask, const float* lse, const float* coef,
+                  const float* grad_output, float* dH, float* dW, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/* GSPO segment stage alone (no GEMM), from given per-token log-probs.
+ *   per segment s with L_s active tokens: rho_s = sum_t m_t (logp_t - old_t) / L_s,
+ *   sigma_s = exp(rho_s), c_s = clip(sigma_s, 1 - eps_low, 1 + eps_high),
+ *   pol_s = -min(sigma_s A_s, c_s A_s); policy_loss = mean of pol_s over the
+ *   S_live segments with L_s > 0; kl = sequence-mean of the token k3 term;
+ *   coef_t = m_t / (S_live L_s) * (-A_s sigma_s [sigma_s A_s <= c_s A_s])
+ *            + beta * m_t / (S_live L_s) * (1 - exp(ref_t - logp_t)).
+ *   seg_mean_logp[s] (may be NULL) = mean active-token logp of segment s, 0 if
+ *   L_s = 0 (the new_logprobs metric).
+ * p->n_tokens, n_seqs, eps_*, beta, ignore_index and validate are used (the GEMM
+ * fields d_model, v_real, v_rows, dtype, inv_tau, reduction and level are ignored);
+ * y is read only when mask is NULL (then it may not be NULL).  Needs
+ * gspo_segment_workspace_size(p) bytes of workspace.
+ * Status 0, 1, 2, 6; with validate also 3, 4, 5. */
+int gspo_segment_reduce(const grpo_head_params* p, const float* logp, const float* old_logp,
+                        const float* ref_logp, const uint8_t* mask, const int64_t* y,
+                        const int32_t* sid, const float* adv, float* out3, float* coef,
+                        float* seg_mean_logp, int32_t* counts, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Bytes of device workspace gspo_segment_reduce needs (per-segment totals and
+ * scalars).  0 if p is invalid. */
+size_t gspo_segment_workspace_size(const grpo_head_params* p);
+
+/* Description of the last non-zero status returned on the calling thread
+ * (thread-local; valid until the next call on that thread).  "" if none. */
+const char* grpo_head_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRPO_HEAD_H */

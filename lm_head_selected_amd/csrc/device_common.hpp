@@ -1,0 +1,63 @@
+// Device-side types and helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gh {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// gfx9 buffer resource word 3 for raw (stride 0) dword-addressed buffers.
+constexpr int kBufferFlags = 0x00020000;
+// A voffset this large is out of range for every resource built here, so a
+// buffer load through it returns zeros and a store through it is dropped.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferFlags);
+}
+
+__device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff) {
+  return __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Element types of the two operand paths.
+template <typename T> struct Elem;
+template <> struct Elem<__bf16> { static constexpr int size = 2; };
+template <> struct Elem<float> { static constexpr int size = 4; };
+
+// XCD-aware tile order.  Workgroups are dispatched round-robin over the 8 XCDs
+// (bid % 8).  Renumber so each XCD receives a contiguous run of logical tile ids;
+// inside a run, tiles walk `group_m` M-tiles down one N-tile before moving to the
+// next N-tile, so workgroups resident together on one XCD share operand slices
+// in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n,
+                                            int group_m, int& tm, int& tn) {
+  const int q = nwg >> 3, r = nwg & 7;
+  const int xcd = bid & 7, idx = bid >> 3;
+  const int logical = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  const int per_group = group_m * tiles_n;
+  const int g = logical / per_group;
+  const int first_m = g * group_m;
+  int gsize = tiles_m - first_m;
+  gsize = gsize < group_m ? gsize : group_m;
+  const int in_g = logical - g * per_group;
+  tm = first_m + in_g % gsize;
+  tn = in_g / gsize;
+}
+
+}  // namespace gh

@@ -1,0 +1,308 @@
+// C ABI of the fused LM-head GRPO / GSPO loss (declared in include/grpo_head.h).
+//
+// Host side only: argument checks (before anything is enqueued), workspace
+// layout, launch sequencing on the caller's stream, the optional validation
+// sync and the thread-local error text.  Failing loudly instead of falling back
+// follows RL-Kernel PR #291 (commit notes: incompatible backends are rejected
+// with explicit reasons and never used as a silent fallback); the validation sync
+// being opt-in follows the same page's review thread on per-call device syncs.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/grpo_head.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return GRPO_HEAD_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(GRPO_HEAD_HIP_ERROR, "%s: %s", where, hipGetErrorString(e));
+}
+
+// Every tile-row block of an operand is addressed with 32-bit buffer offsets.
+constexpr int64_t kMaxRowBytes = (int64_t(1) << 31) / 256 - 1;
+
+int check_common(const grpo_head_params* p, bool need_gemm) {
+  if (!p) return fail(GRPO_HEAD_INVALID_ARGUMENT, "params is NULL");
+  if (p->n_tokens < 0) return fail(GRPO_HEAD_INVALID_ARGUMENT, "n_tokens < 0");
+  if (p->n_tokens > (int64_t(1) << 31) - 1)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "n_tokens above 2^31 - 1");
+  if (p->n_seqs < 0 || (p->n_tokens > 0 && p->n_seqs < 1))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "n_seqs must be >= 1 when n_tokens > 0");
+  if (p->n_seqs > (int64_t(1) << 31) - 1) return fail(GRPO_HEAD_INVALID_ARGUMENT, "n_seqs too large");
+  if (p->level != GRPO_HEAD_LEVEL_TOKEN && p->level != GRPO_HEAD_LEVEL_SEQUENCE_GSPO)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "unknown level %d", p->level);
+  if (p->reduction != GRPO_HEAD_TOKEN_MEAN && p->reduction != GRPO_HEAD_SEQUENCE_MEAN)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "unknown reduction %d", p->reduction);
+  if (!(p->eps_low >= 0.0f && p->eps_low < 1.0f))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "eps_low must be in [0, 1)");
+  if (!(p->eps_high >= 0.0f) || !std::isfinite(p->eps_high))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "eps_high must be finite and >= 0");
+  if (!(p->beta >= 0.0f) || !std::isfinite(p->beta))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "beta must be finite and >= 0");
+  if (p->validate != 0 && p->validate != 1)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "validate must be 0 or 1");
+  if (!need_gemm) return GRPO_HEAD_OK;
+  if (p->dtype != GRPO_HEAD_BF16 && p->dtype != GRPO_HEAD_F32)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "unknown dtype %d", p->dtype);
+  if (p->d_model <= 0 || p->d_model % 64 != 0)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "d_model must be a positive multiple of 64 (got %lld)",
+                (long long)p->d_model);
+  if (p->v_real < 1) return fail(GRPO_HEAD_INVALID_ARGUMENT, "v_real must be >= 1");
+  if (p->v_rows < p->v_real) return fail(GRPO_HEAD_INVALID_ARGUMENT, "v_rows < v_real");
+  if (!(p->inv_tau > 0.0f) || !std::isfinite(p->inv_tau))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "inv_tau must be finite and > 0");
+  if (p->chunk_tokens < 0) return fail(GRPO_HEAD_INVALID_ARGUMENT, "chunk_tokens < 0");
+  const int64_t esz = p->dtype == GRPO_HEAD_BF16 ? 2 : 4;
+  const int64_t vk = gh::ceil_div(p->v_real, gh::kVocabTile) * gh::kVocabTile;
+  if (p->d_model * esz > kMaxRowBytes || vk * esz > kMaxRowBytes ||
+      gh::ceil_div(p->n_tokens, gh::kTokenTile) * gh::kTokenTile * esz > kMaxRowBytes)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "a row of an operand exceeds %lld bytes",
+                (long long)kMaxRowBytes);
+  if (gh::ceil_div(p->v_real, gh::kVocabTile) * gh::ceil_div(p->n_tokens, gh::kTokenTile) >
+      (int64_t(1) << 31) - 1)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "problem too large for one launch");
+  return GRPO_HEAD_OK;
+}
+
+gh::WsLayout layout(const grpo_head_params* p, bool with_gemm = true) {
+  gh::WsLayout L;
+  const int64_t N = p->n_tokens, S = p->n_seqs, D = p->d_model;
+  const int64_t esz = p->dtype == GRPO_HEAD_F32 ? 4 : 2;
+  L.n_vt = (with_gemm && p->v_real > 0) ? gh::ceil_div(p->v_real, gh::kVocabTile) : 0;
+  L.v_k = L.n_vt * gh::kVocabTile;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = gh::align_up(off + bytes); return o; };
+  L.partials = take((size_t)L.n_vt * N * 8);
+  L.zy = take(with_gemm ? (size_t)N * 4 : 0);
+  L.seq_L = take((size_t)S * 4);
+  L.seq_F = take((size_t)S * 16);
+  L.seq_G = take((size_t)S * 4);
+  L.scal = take(64);
+  L.flags = take(64);
+  L.fwd_bytes = off;
+  if (!with_gemm) return L;
+
+  int64_t chunk = p->chunk_tokens > 0 ? p->chunk_tokens : N;
+  if (chunk > N) chunk = N;
+  chunk = gh::ceil_div(chunk > 0 ? chunk : 1, gh::kTokenTile) * gh::kTokenTile;
+  L.chunk = chunk;
+  off = 0;
+  L.bflags = take(64);
+  L.wt = take((size_t)D * L.v_k * esz);
+  L.ht = take((size_t)D * chunk * esz);
+  L.dz = take((size_t)chunk * L.v_k * esz);
+  L.dzt = take((size_t)L.v_k * chunk * esz);
+  L.bwd_bytes = off > L.fwd_bytes ? off : L.fwd_bytes;
+  return L;
+}
+
+// Tile-order group sizes (M-tiles walked per N-tile), chosen by measurement.
+constexpr int kGroupFwd = 8, kGroupDh = 16, kGroupDw = 16;
+
+int finish_validation(uint32_t* dflags, hipStream_t s, bool check_active) {
+  uint32_t h[2] = {0, 0};
+  hipError_t e = hipMemcpyAsync(h, dflags, sizeof h, hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "validation copy");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "validation sync");
+  if (h[0] & (gh::kFlagTarget | gh::kFlagSid))
+    return fail(GRPO_HEAD_TARGET_OUT_OF_RANGE, "%s",
+                (h[0] & gh::kFlagTarget) ? "an active target is outside [0, v_real)"
+                                         : "sid is decreasing or outside [0, n_seqs)");
+  if (check_active && h[1] == 0) return fail(GRPO_HEAD_NO_ACTIVE_TOKENS, "no active token");
+  if (h[0] & gh::kFlagNonfinite) return fail(GRPO_HEAD_NONFINITE, "non-finite value");
+  return ok();
+}
+
+int run_loss(const grpo_head_params* p, const gh::WsLayout& L, char* ws, const float* logp,
+             const float* old_logp, const float* ref_logp, const uint8_t* mask,
+             const int64_t* y, const int32_t* sid, const float* adv, float* out3, float* coef,
+             int32_t* counts, float* seg_mean, hipStream_t s) {
+  gh::LossArgs la{};
+  la.n_tokens = p->n_tokens;
+  la.n_seqs = p->n_seqs;
+  la.level = p->level;
+  la.reduction = p->reduction;
+  la.eps_low = p->eps_low;
+  la.eps_high = p->eps_high;
+  la.beta = p->beta;
+  la.logp = logp;
+  la.old_logp = old_logp;
+  la.ref_logp = ref_logp;
+  la.adv = adv;
+  la.sid = sid;
+  la.mask = mask;
+  la.y = y;
+  la.ignore_index = p->ignore_index;
+  la.seq_L = (int32_t*)(ws + L.seq_L);
+  la.seq_F = (float*)(ws + L.seq_F);
+  la.seq_G = (float*)(ws + L.seq_G);
+  la.scal = (float*)(ws + L.scal);
+  la.out3 = out3;
+  la.coef = coef;
+  la.counts = counts;
+  la.seg_mean = seg_mean;
+  hipError_t e = gh::launch_loss(la, s);
+  if (e != hipSuccess) return hip_fail(e, "objective kernels");
+  return GRPO_HEAD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t grpo_head_fwd_workspace_size(const grpo_head_params* p) {
+  if (check_common(p, true) != GRPO_HEAD_OK) return 0;
+  return layout(p).fwd_bytes;
+}
+
+size_t grpo_head_workspace_size(const grpo_head_params* p) {
+  if (check_common(p, true) != GRPO_HEAD_OK) return 0;
+  return layout(p).bwd_bytes;
+}
+
+size_t gspo_segment_workspace_size(const grpo_head_params* p) {
+  if (check_common(p, false) != GRPO_HEAD_OK) return 0;
+  return layout(p, false).fwd_bytes;
+}
+
+const char* grpo_head_last_error(void) { return g_last_error.c_str(); }
+
+int grpo_head_fwd(const grpo_head_params* p, const void* H, const void* W, const int64_t* y,
+                  const uint8_t* mask, const int32_t* sid, const float* adv,
+                  const float* old_logp, const float* ref_logp, float* logp, float* lse,
+                  float* out3, float* coef, int32_t* counts, void* ws, size_t ws_bytes,
+                  void* stream) {
+  int rc = check_common(p, true);
+  if (rc) return rc;
+  if (!out3) return fail(GRPO_HEAD_INVALID_ARGUMENT, "out3 is NULL");
+  if (p->n_seqs > 0 && (!adv || !counts))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "adv and counts must not be NULL");
+  if (p->n_tokens > 0 && (!H || !W || !y || !sid || !old_logp || !logp || !lse || !coef))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "a required buffer is NULL");
+  if (p->beta > 0.0f && p->n_tokens > 0 && !ref_logp)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "beta > 0 needs ref_logp");
+  const gh::WsLayout L = layout(p);
+  if (!ws || ws_bytes < L.fwd_bytes)
+    return fail(GRPO_HEAD_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes,
+                L.fwd_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  hipError_t e;
+  if (p->n_tokens > 0) {
+    gh::FwdTileArgs fa{W, H, y, mask, p->n_tokens, p->d_model, p->v_real, p->ignore_index,
+                       p->inv_tau, (float2*)(w + L.partials), (float*)(w + L.zy), kGroupFwd};
+    e = gh::launch_fwd_tiles(p->dtype, fa, L.n_vt, s);
+    if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
+    gh::MergeArgs ma{(const float2*)(w + L.partials), (const float*)(w + L.zy), y, mask,
+                     p->n_tokens, L.n_vt, p->v_real, p->ignore_index, logp, lse};
+    e = gh::launch_merge(ma, s);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel");
+  }
+  rc = run_loss(p, L, w, logp, old_logp, ref_logp, mask, y, sid, adv, out3, coef, counts,
+                nullptr, s);
+  if (rc) return rc;
+  if (p->validate) {
+    gh::ValidateArgs va{p->n_tokens, p->n_seqs, p->v_real, p->ignore_index, y, mask, sid,
+                        lse, logp, old_logp, ref_logp, out3, (uint32_t*)(w + L.flags)};
+    e = gh::launch_validate(va, s);
+    if (e != hipSuccess) return hip_fail(e, "validation kernel");
+    return finish_validation((uint32_t*)(w + L.flags), s, true);
+  }
+  return ok();
+}
+
+int grpo_head_bwd(const grpo_head_params* p, const void* H, const void* W, const int64_t* y,
+                  const uint8_t* mask, const float* lse, const float* coef,
+                  const float* grad_output, float* dH, float* dW, void* ws, size_t ws_bytes,
+                  void* stream) {
+  int rc = check_common(p, true);
+  if (rc) return rc;
+  if (!W || !dW) return fail(GRPO_HEAD_INVALID_ARGUMENT, "W and dW must not be NULL");
+  if (p->n_tokens > 0 && (!H || !y || !lse || !coef || !dH))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "a required buffer is NULL");
+  if (p->n_tokens > 0 && !mask && !y)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "y is needed without a mask");
+  const gh::WsLayout L = layout(p);
+  if (!ws || ws_bytes < L.bwd_bytes)
+    return fail(GRPO_HEAD_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes,
+                L.bwd_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  gh::BwdArgs ba{H, W, y, mask, lse, coef, grad_output, dH, dW, p->n_tokens, p->d_model,
+                 p->v_real, p->v_rows, p->ignore_index, p->inv_tau, w, &L,
+                 kGroupFwd, kGroupDh, kGroupDw};
+  hipError_t e = gh::launch_bwd(p->dtype, ba, s);
+  if (e != hipSuccess) return hip_fail(e, "backward kernels");
+  if (p->validate) {
+    gh::ValidateArgs va{p->n_tokens, p->n_seqs > 0 ? p->n_seqs : 1, p->v_real, p->ignore_index,
+                        y, mask, nullptr, lse, coef, nullptr, nullptr, nullptr,
+                        (uint32_t*)(w + L.bflags)};
+    e = gh::launch_validate(va, s);
+    if (e != hipSuccess) return hip_fail(e, "validation kernel");
+    return finish_validation((uint32_t*)(w + L.bflags), s, false);
+  }
+  return ok();
+}
+
+int gspo_segment_reduce(const grpo_head_params* p, const float* logp, const float* old_logp,
+                        const float* ref_logp, const uint8_t* mask, const int64_t* y,
+                        const int32_t* sid, const float* adv, float* out3, float* coef,
+                        float* seg_mean_logp, int32_t* counts, void* ws, size_t ws_bytes,
+                        void* stream) {
+  int rc = check_common(p, false);
+  if (rc) return rc;
+  if (!out3) return fail(GRPO_HEAD_INVALID_ARGUMENT, "out3 is NULL");
+  if (p->n_seqs > 0 && (!adv || !counts))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "adv and counts must not be NULL");
+  if (p->n_tokens > 0 && (!logp || !old_logp || !sid || !coef))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "a required buffer is NULL");
+  if (p->n_tokens > 0 && !mask && !y)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "y is needed without a mask");
+  if (p->beta > 0.0f && p->n_tokens > 0 && !ref_logp)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "beta > 0 needs ref_logp");
+  grpo_head_params q = *p;
+  q.level = GRPO_HEAD_LEVEL_SEQUENCE_GSPO;
+  const gh::WsLayout L = layout(&q, false);
+  if (!ws || ws_bytes < L.fwd_bytes)
+    return fail(GRPO_HEAD_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes,
+                L.fwd_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  rc = run_loss(&q, L, w, logp, old_logp, ref_logp, mask, y, sid, adv, out3, coef, counts,
+                seg_mean_logp, s);
+  if (rc) return rc;
+  if (p->validate) {
+    gh::ValidateArgs va{p->n_tokens, p->n_seqs, p->v_real, p->ignore_index, y, mask, sid,
+                        nullptr, logp, old_logp, ref_logp, out3, (uint32_t*)(w + L.flags)};
+    va.check_targets = 0;
+    hipError_t e = gh::launch_validate(va, s);
+    if (e != hipSuccess) return hip_fail(e, "validation kernel");
+    return finish_validation((uint32_t*)(w + L.flags), s, true);
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Host-side launch interface between the C ABI and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gh {
+
+constexpr int64_t kVocabTile = 256;   // vocabulary rows per forward/backward tile
+constexpr int64_t kTokenTile = 256;   // tokens per tile
+constexpr size_t kAlign = 256;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Byte offsets into the caller's workspace.
+struct WsLayout {
+  // forward / segment stage
+  size_t partials = 0, zy = 0, seq_L = 0, seq_F = 0, seq_G = 0, scal = 0, flags = 0;
+  size_t fwd_bytes = 0;
+  // backward (reuses the workspace from offset 0)
+  size_t bflags = 0, wt = 0, ht = 0, dz = 0, dzt = 0;
+  size_t bwd_bytes = 0;
+  int64_t n_vt = 0;        // vocabulary tiles covering [0, v_real)
+  int64_t v_k = 0;         // n_vt * 256: vocabulary extent of the staging buffers
+  int64_t chunk = 0;       // tokens per backward chunk (multiple of 256)
+};
+
+// Validation flags (bit set in the flags word)
+enum : uint32_t { kFlagTarget = 1u, kFlagNonfinite = 2u, kFlagSid = 4u };
+
+struct FwdTileArgs {
+  const void* W; const void* H; const int64_t* y; const uint8_t* mask;
+  int64_t n_tokens, d_model, v_real, ignore_index;
+  float inv_tau;
+  float2* partials;  // [n_vt][n_tokens]
+  float* zy;         // [n_tokens]
+  int group_m;
+};
+struct MergeArgs {
+  const float2* partials; const float* zy; const int64_t* y; const uint8_t* mask;
+  int64_t n_tokens, n_vt, v_real, ignore_index;
+  float* logp; float* lse;
+};
+struct LossArgs {
+  int64_t n_tokens; int64_t n_seqs; int32_t level, reduction;
+  float eps_low, eps_high, beta;
+  const float* logp; const float* old_logp; const float* ref_logp; const float* adv;
+  const int32_t* sid; const uint8_t* mask; const int64_t* y; int64_t ignore_index;
+  int32_t* seq_L; float* seq_F; float* seq_G; float* scal;
+  float* out3; float* coef; int32_t* counts; float* seg_mean;
+};
+struct ValidateArgs {
+  int64_t n_tokens, n_seqs, v_real, ignore_index;
+  const int64_t* y; const uint8_t* mask; const int32_t* sid;
+  const float* a; const float* b; const float* c; const float* d;  // checked if non-null
+  const float* out3;
+  uint32_t* flags;  // [0] = flag bits, [1] = active-token count
+  int check_targets = 1;  // check active targets against [0, v_real)
+};
+struct BwdArgs {
+  const void* H; const void* W; const int64_t* y; const uint8_t* mask;
+  const float* lse; const float* coef; const float* grad_output;
+  float* dH; float* dW;
+  int64_t n_tokens, d_model, v_real, v_rows, ignore_index;
+  float inv_tau;
+  char* ws; const WsLayout* L;
+  int group_fwd, group_dh, group_dw;
+};
+
+hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_loss(const LossArgs& a, hipStream_t s);
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
+hipError_t launch_bwd(int dtype, const BwdArgs& a, hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace gh

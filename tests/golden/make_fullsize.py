@@ -1,0 +1,54 @@
+"""Write the fp64 oracle's selected log-prob and LSE for the full-size workloads.
+
+Calls only the oracle and the seeded generators.  Usage (from the repo root):
+    python tests/golden/make_fullsize.py [config index ...]      # default: 3 4
+Each output file records a fingerprint of the regenerated inputs so readers can
+check they rebuilt the same workload.
+"""
+import hashlib
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from synth import CONFIGS, make_inputs  # noqa: E402
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def fingerprint(inp: dict) -> str:
+    h = hashlib.sha256()
+    for k in ("H", "y", "sid", "adv", "noise_old"):
+        h.update(np.ascontiguousarray(inp[k]).tobytes())
+    h.update(np.ascontiguousarray(inp["W"][:: 97]).tobytes())
+    if inp["mask"] is not None:
+        h.update(inp["mask"].tobytes())
+    if inp["noise_ref"] is not None:
+        h.update(inp["noise_ref"].tobytes())
+    return h.hexdigest()
+
+
+def path_for(index: int) -> str:
+    return os.path.join(HERE, f"fullsize_{CONFIGS[index].name}.npz")
+
+
+def main(indices):
+    for i in indices:
+        cfg = CONFIGS[i]
+        t0 = time.time()
+        inp = make_inputs(cfg)
+        act = oracle.active_tokens(inp["y"], inp["mask"], inp["ignore_index"])
+        logp, lse = oracle.forward(inp["H"], inp["W"], inp["y"], act, inp["v_real"],
+                                   inp["inv_tau"], inp["dtype"], block=256)
+        np.savez_compressed(path_for(i), logp=logp, lse=lse,
+                            fingerprint=np.array(fingerprint(inp)))
+        print(f"{cfg.name}: {time.time() - t0:.1f} s", flush=True)
+
+
+if __name__ == "__main__":
+    main([int(a) for a in sys.argv[1:]] or [3, 4])

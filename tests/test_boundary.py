@@ -1,0 +1,118 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every
+function include/grpo_head.h declares, and rejects bad arguments on the host
+before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+gb = pytest.importorskip("lm_head_selected_amd.binding",
+                         reason="libgrpo_head.so not built (run __graft_entry__.build())")
+
+HEADER = os.path.join(ROOT, "include", "grpo_head.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if"})
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(gb.EXPORTS), names
+    lib = ctypes.CDLL(gb.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_params_struct_layout_matches_header():
+    # 7 int64 + 4 int32 + 4 float, no padding
+    assert ctypes.sizeof(gb.Params) == 7 * 8 + 4 * 4 + 4 * 4
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct grpo_head_params \{(.*?)\}", text, re.S).group(1)
+    fields = re.findall(r"\b(\w+);", body)
+    assert fields == [f[0] for f in gb.Params._fields_]
+
+
+def P(**kw):
+    base = dict(n_tokens=1024, d_model=1024, v_real=4096, v_rows=4096, n_seqs=8, dtype="bf16",
+                reduction="sequence_mean", inv_tau=1.0, eps_low=0.2, eps_high=0.2, beta=0.1)
+    base.update(kw)
+    return gb.make_params(**base)
+
+
+def test_workspace_sizes():
+    p = P()
+    fwd = gb.fwd_workspace_size(p)
+    full = gb.workspace_size(p)
+    # partials: 16 tiles x 1024 tokens x 8 B dominate the forward workspace
+    assert fwd >= 16 * 1024 * 8
+    # backward: W^T + H^T chunk + dlogits + its transpose, bf16
+    assert full >= (1024 * 4096 + 1024 * 1024 + 2 * 1024 * 4096) * 2
+    assert full >= fwd
+    # fp32 path doubles the staging buffers
+    assert gb.workspace_size(P(dtype="f32")) > full
+    # chunking bounds the backward workspace
+    assert gb.workspace_size(P(chunk_tokens=256)) < full
+    assert gb.segment_workspace_size(P(d_model=0)) > 0
+
+
+@pytest.mark.parametrize("bad", [dict(d_model=100), dict(d_model=0), dict(v_real=0),
+                                 dict(v_rows=10), dict(n_seqs=0), dict(n_tokens=-1),
+                                 dict(dtype=7), dict(reduction=5), dict(level=3),
+                                 dict(inv_tau=0.0), dict(eps_low=1.0), dict(eps_low=-0.1),
+                                 dict(beta=-1.0), dict(inv_tau=float("nan")),
+                                 dict(chunk_tokens=-5)])
+def test_invalid_params_rejected_without_gpu(bad):
+    p = P(**bad)
+    assert gb.workspace_size(p) == 0
+    with pytest.raises(gb.GrpoHeadError) as e:
+        gb.grpo_head_fwd(p, 1, 1, 1, None, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, ws_bytes=1 << 40,
+                         stream=0)
+    assert e.value.status == 1
+    assert gb.lib.grpo_head_last_error().decode()
+
+
+def test_null_buffers_rejected():
+    p = P()
+    with pytest.raises(gb.GrpoHeadError) as e:   # out3 NULL
+        gb.grpo_head_fwd(p, 1, 1, 1, None, 1, 1, 1, 1, 1, 1, None, 1, 1, 1, ws_bytes=1 << 40,
+                         stream=0)
+    assert e.value.status == 1
+    with pytest.raises(gb.GrpoHeadError) as e:   # beta > 0 without ref_logp
+        gb.grpo_head_fwd(p, 1, 1, 1, None, 1, 1, 1, None, 1, 1, 1, 1, 1, 1, ws_bytes=1 << 40,
+                         stream=0)
+    assert e.value.status == 1 and "ref_logp" in str(e.value)
+    with pytest.raises(gb.GrpoHeadError) as e:   # dW NULL
+        gb.grpo_head_bwd(p, 1, 1, 1, None, 1, 1, None, 1, None, 1, ws_bytes=1 << 40, stream=0)
+    assert e.value.status == 1
+
+
+def test_workspace_too_small_rejected():
+    p = P()
+    need = gb.fwd_workspace_size(p)
+    with pytest.raises(gb.GrpoHeadError) as e:
+        gb.grpo_head_fwd(p, 1, 1, 1, None, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, ws_bytes=need - 1,
+                         stream=0)
+    assert e.value.status == 2
+    with pytest.raises(gb.GrpoHeadError) as e:
+        gb.grpo_head_bwd(p, 1, 1, 1, None, 1, 1, None, 1, 1, 1,
+                         ws_bytes=gb.workspace_size(p) - 1, stream=0)
+    assert e.value.status == 2
+    q = P(level="sequence_gspo")
+    with pytest.raises(gb.GrpoHeadError) as e:
+        gb.gspo_segment_reduce(q, 1, 1, 1, None, 1, 1, 1, 1, 1, None, 1, 1,
+                               ws_bytes=gb.segment_workspace_size(q) - 1, stream=0)
+    assert e.value.status == 2
+
+
+def test_segment_reduce_needs_targets_without_mask():
+    q = P(level="sequence_gspo", beta=0.0)
+    with pytest.raises(gb.GrpoHeadError) as e:
+        gb.gspo_segment_reduce(q, 1, 1, None, None, None, 1, 1, 1, 1, None, 1, 1,
+                               ws_bytes=1 << 30, stream=0)
+    assert e.value.status == 1 and "mask" in str(e.value)
