@@ -24,7 +24,12 @@ STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "WORKSPACE_TOO_SMALL", 3: "NO_ACTIV
 
 EXPORTS = ("grpo_head_fwd_workspace_size", "grpo_head_workspace_size",
            "gspo_segment_workspace_size", "grpo_head_fwd", "grpo_head_bwd",
-           "gspo_segment_reduce", "grpo_head_last_error")
+           "gspo_segment_reduce", "grpo_head_set_stage_events", "grpo_head_last_error")
+
+# stage-event slots recorded by grpo_head_fwd / grpo_head_bwd
+STAGES = {"fwd_tiles": (0, 1), "fwd_merge": (1, 2), "fwd_objective": (2, 3),
+          "bwd_w_transpose": (4, 5), "bwd_dlogits": (5, 6), "bwd_dh": (6, 7),
+          "bwd_transposes": (7, 8), "bwd_dw": (8, 9)}
 
 
 class GrpoHeadError(RuntimeError):
@@ -61,6 +66,8 @@ def _load():
     lib.grpo_head_bwd.restype = i32
     lib.gspo_segment_reduce.argtypes = [pp] + [vp] * 11 + [vp, sz, vp]
     lib.gspo_segment_reduce.restype = i32
+    lib.grpo_head_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
+    lib.grpo_head_set_stage_events.restype = i32
     lib.grpo_head_last_error.argtypes = []
     lib.grpo_head_last_error.restype = ctypes.c_char_p
     return lib
@@ -102,6 +109,17 @@ def _stream(stream):
 def _check(rc: int):
     if rc != 0:
         raise GrpoHeadError(rc, lib.grpo_head_last_error().decode())
+
+
+def set_stage_events(events) -> None:
+    """Record the given torch.cuda.Event objects (or raw handles / None) at stage
+    boundaries of later fwd/bwd calls; None switches timing off."""
+    if events is None:
+        _check(lib.grpo_head_set_stage_events(None, 0))
+        return
+    raw = [None if e is None else (e if isinstance(e, int) else e.cuda_event) for e in events]
+    arr = (ctypes.c_void_p * len(raw))(*raw)
+    _check(lib.grpo_head_set_stage_events(arr, len(raw)))
 
 
 def fwd_workspace_size(p: Params) -> int:

@@ -213,6 +213,7 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   }
   // WT[d][v] = W[v][d] for v < v_real, 0 up to v_k
   transpose<E>(a.W, D, a.v_real, D, wt, D, VK, s);
+  const StageEvents& ev = *a.marks;
 
   const int tiles_v = (int)L.n_vt;
   const int tiles_d = (int)ceil_div(D, kTile);
@@ -220,22 +221,26 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     const int64_t nc = (N - c0) < L.chunk ? (N - c0) : L.chunk;
     const int64_t ncp = ceil_div(nc, kTokenTile) * kTokenTile;
     const int tiles_t = (int)(ncp / kTokenTile);
+    ev.mark(5, s);
 
     DlogitsArgs d{a.W, (const char*)a.H + c0 * D * esz, a.y + c0,
                   a.mask ? a.mask + c0 : nullptr, a.lse + c0, a.coef + c0, a.grad_output,
                   nc, D, a.v_real, VK, a.ignore_index, a.inv_tau, dz, a.group_fwd};
     hipLaunchKernelGGL(dlogits_kernel<T>, dim3(tiles_v * tiles_t), dim3(kThreads), 0, s, d,
                        tiles_v, tiles_t);
+    ev.mark(6, s);
 
     // dH rows of the chunk: M = d (WT rows), N = t (dz rows), K = v
     ProductArgs ph{Operand{wt, VK * esz, D}, Operand{dz, VK * esz, nc}, VK * esz,
                    a.dH + c0 * D, D, D, nc, INT64_MAX, 0, a.group_dh};
     hipLaunchKernelGGL(product_kernel<T>, dim3(tiles_d * tiles_t), dim3(kThreads), 0, s, ph,
                        tiles_d, tiles_t);
+    ev.mark(7, s);
 
     // transposes for dW: dzT[v][t] and HT[d][t]
     transpose<E>(dz, VK, nc, VK, dzt, VK, ncp, s);
     transpose<E>((const char*)a.H + c0 * D * esz, D, nc, D, ht, D, ncp, s);
+    ev.mark(8, s);
 
     // dW: M = d (HT rows), N = v (dzT rows), K = t
     ProductArgs pw{Operand{ht, ncp * esz, D}, Operand{dzt, ncp * esz, VK}, ncp * esz,
@@ -243,6 +248,7 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
                    a.group_dw};
     hipLaunchKernelGGL(product_kernel<T>, dim3(tiles_d * tiles_v), dim3(kThreads), 0, s, pw,
                        tiles_d, tiles_v);
+    ev.mark(9, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -19,6 +19,7 @@
 namespace {
 
 thread_local std::string g_last_error;
+gh::StageEvents g_marks;  // stage timing events (grpo_head_set_stage_events)
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {
@@ -190,6 +191,18 @@ size_t gspo_segment_workspace_size(const grpo_head_params* p) {
 
 const char* grpo_head_last_error(void) { return g_last_error.c_str(); }
 
+int grpo_head_set_stage_events(void* const* events, int n_events) {
+  if (n_events < 0 || n_events > 16)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "n_events must be in [0, 16]");
+  gh::StageEvents m;
+  if (events) {
+    for (int i = 0; i < n_events; ++i) m.ev[i] = events[i];
+    m.n = n_events;
+  }
+  g_marks = m;
+  return ok();
+}
+
 int grpo_head_fwd(const grpo_head_params* p, const void* H, const void* W, const int64_t* y,
                   const uint8_t* mask, const int32_t* sid, const float* adv,
                   const float* old_logp, const float* ref_logp, float* logp, float* lse,
@@ -212,18 +225,22 @@ int grpo_head_fwd(const grpo_head_params* p, const void* H, const void* W, const
   char* w = (char*)ws;
   hipError_t e;
   if (p->n_tokens > 0) {
+    g_marks.mark(0, s);
     gh::FwdTileArgs fa{W, H, y, mask, p->n_tokens, p->d_model, p->v_real, p->ignore_index,
                        p->inv_tau, (float2*)(w + L.partials), (float*)(w + L.zy), kGroupFwd};
     e = gh::launch_fwd_tiles(p->dtype, fa, L.n_vt, s);
     if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
+    g_marks.mark(1, s);
     gh::MergeArgs ma{(const float2*)(w + L.partials), (const float*)(w + L.zy), y, mask,
                      p->n_tokens, L.n_vt, p->v_real, p->ignore_index, logp, lse};
     e = gh::launch_merge(ma, s);
     if (e != hipSuccess) return hip_fail(e, "merge kernel");
+    g_marks.mark(2, s);
   }
   rc = run_loss(p, L, w, logp, old_logp, ref_logp, mask, y, sid, adv, out3, coef, counts,
                 nullptr, s);
   if (rc) return rc;
+  if (p->n_tokens > 0) g_marks.mark(3, s);
   if (p->validate) {
     gh::ValidateArgs va{p->n_tokens, p->n_seqs, p->v_real, p->ignore_index, y, mask, sid,
                         lse, logp, old_logp, ref_logp, out3, (uint32_t*)(w + L.flags)};
@@ -251,9 +268,10 @@ int grpo_head_bwd(const grpo_head_params* p, const void* H, const void* W, const
                 L.bwd_bytes);
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
+  g_marks.mark(4, s);
   gh::BwdArgs ba{H, W, y, mask, lse, coef, grad_output, dH, dW, p->n_tokens, p->d_model,
                  p->v_real, p->v_rows, p->ignore_index, p->inv_tau, w, &L,
-                 kGroupFwd, kGroupDh, kGroupDw};
+                 kGroupFwd, kGroupDh, kGroupDw, &g_marks};
   hipError_t e = gh::launch_bwd(p->dtype, ba, s);
   if (e != hipSuccess) return hip_fail(e, "backward kernels");
   if (p->validate) {

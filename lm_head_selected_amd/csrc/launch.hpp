@@ -59,6 +59,15 @@ struct ValidateArgs {
   uint32_t* flags;  // [0] = flag bits, [1] = active-token count
   int check_targets = 1;  // check active targets against [0, v_real)
 };
+// Optional stage-boundary events (see grpo_head_set_stage_events).
+struct StageEvents {
+  void* ev[16] = {};
+  int n = 0;
+  void mark(int i, hipStream_t s) const {
+    if (i < n && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
+  }
+};
+
 struct BwdArgs {
   const void* H; const void* W; const int64_t* y; const uint8_t* mask;
   const float* lse; const float* coef; const float* grad_output;
@@ -67,6 +76,7 @@ struct BwdArgs {
   float inv_tau;
   char* ws; const WsLayout* L;
   int group_fwd, group_dh, group_dw;
+  const StageEvents* marks;
 };
 
 hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt, hipStream_t s);
