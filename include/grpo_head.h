@@ -207,11 +207,12 @@ size_t gspo_segment_workspace_size(const grpo_head_params* p);
  * hipEvent_t handles (cast to void*; NULL entries are skipped), or events == NULL
  * to switch timing off.  The array is copied.  While set, the calls record
  * events on their stream at stage boundaries:
- *   grpo_head_fwd: [0] before the tile kernel, [1] after it, [2] after the merge,
- *                  [3] after the objective stage;
+ *   grpo_head_fwd: [0] before the tile kernels, [1] after them, [2] after the
+ *                  target-logit gather and the merge, [3] after the objective
+ *                  stage;
  *   grpo_head_bwd: [4] at entry, [5] at each token chunk's start (after the
  *                  transpose of W for the first chunk), [6] after the dlogits
- *                  kernel, [7] after the dH product, [8] after the two
+ *                  kernels, [7] after the dH product, [8] after the two
  *                  transposes, [9] after the dW product (with several chunks,
  *                  [5]-[9] describe the last one).
  * Returns GRPO_HEAD_INVALID_ARGUMENT if n_events < 0 or > 16. */

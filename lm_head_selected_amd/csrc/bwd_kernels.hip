@@ -4,16 +4,22 @@
 //   G[t, v] = grad_output * coef_t * (1[v == y_t] - exp(z[t, v] - lse_t)) / tau
 // (softmax recovered from the logits and the LSE, RL-Kernel PR #291, review
 // thread on the saved fp32 logits; here the logits are recomputed per tile rather
-// than saved).  Padded columns and inactive tokens give 0.
+// than saved).  Inactive tokens give 0.
 //
 // Per token chunk, in ascending chunk order:
-//   1. dlogits_kernel : G tile on the matrix cores -> staging buffer dz[t][v]
-//                       (bf16, nearest-even, on the bf16 path; fp32 on the fp32 path)
-//   2. transpose      : dz -> dzT[v][t] and H chunk -> HT[d][t]
-//   3. dh_kernel      : dH[t][:] = dz[t][:] . W      as (W^T)(dz)^T  on WT[d][v]
-//   4. dw_kernel      : dW[v][:] (+)= dzT[v][:] . H  as (H^T)(dzT)^T on HT[d][t]
+//   1. dlogits_prep_kernel: (g_t, lse_t log2 e) per token
+//   2. dlogits_kernel     : -g_t p_tv tile on the matrix cores -> dz (bf16, nearest
+//                           even, on the bf16 path; fp32 on the fp32 path)
+//      target_logit_kernel: rewrites dz[t][y_t] = g_t (1 - p_t,y_t)
+//   3. product_kernel     : dH[t][:] = dz[t][:] . W      as (W^T)(dz)^T
+//   4. transposes         : dzT[v][t] and HT[d][t]
+//   5. product_kernel     : dW[v][:] (+)= dzT[v][:] . H  as (H^T)(dzT)^T
 // Every product is an NT contraction (both operands contiguous along K) run by
-// the same 256x256 tile core.  WT[d][v] is built once per call.
+// the same tile core.  The staging buffers WT, HT, dz and dzT use the core's
+// K-panel layout (each 256-row tile's K stages stored back to back); WT is built
+// once per call.
+#include <type_traits>
+
 #include "gemm_tile.hpp"
 #include "launch.hpp"
 
@@ -39,15 +45,32 @@ template <> struct Store4<float> {
 
 struct DlogitsArgs {
   const void* W; const void* H;   // H already offset to the chunk's first token
-  const int64_t* y; const uint8_t* mask; const float* lse; const float* coef;
-  const float* grad_output;
+  const float2* gl;               // per chunk token: (g_t, lse_t * log2 e); g_t = 0 if inactive
   int64_t chunk_tokens;           // valid tokens in this chunk
-  int64_t d_model, v_real, v_k, ignore_index;
+  int64_t d_model, v_real, v_k;
   float inv_tau;
-  void* dz;                       // [chunk_pad][v_k]
+  void* dz;                       // K-panel [chunk_pad][v_k]
   int group_m;
 };
 
+// g_t = grad_output * coef_t / tau for active tokens (0 otherwise) and lse_t in
+// base-2 units, for the chunk's tokens.
+__global__ __launch_bounds__(256) void dlogits_prep_kernel(const int64_t* y, const uint8_t* mask,
+                                                           int64_t ignore_index, const float* coef,
+                                                           const float* lse,
+                                                           const float* grad_output, float inv_tau,
+                                                           int64_t n, float2* gl) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  const bool act = token_is_active(mask, y, ignore_index, t);
+  const float gout = grad_output ? *grad_output : 1.0f;
+  gl[t] = make_float2(act ? gout * coef[t] * inv_tau : 0.0f, lse[t] * kLog2e);
+}
+
+// dz[t][v] = -g_t p_tv over the tile (the target element is rewritten afterwards
+// by the target-logit kernel).  Columns of padded vocabulary rows hold finite
+// values that the products never use: they meet zero rows of W^T in dH and the
+// padded rows of dW are written as zeros.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int tiles_m,
                                                            int tiles_n) {
@@ -56,46 +79,40 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, a.group_m, tm, tn);
   const int64_t v0 = (int64_t)tm * kTile, t0 = (int64_t)tn * kTile;
   const int64_t esz = Elem<T>::size;
-  Operand A{(const char*)a.W, a.d_model * esz, a.v_real};
-  Operand B{(const char*)a.H, a.d_model * esz, a.chunk_tokens};
-  f32x16 acc[4][4];
+  const Operand A = row_major(a.W, a.d_model * esz, a.v_real);
+  const Operand B = row_major(a.H, a.d_model * esz, a.chunk_tokens);
+  f32x16 acc[kBI][kBJ];
   zero_acc(acc);
-  gemm_tile<T>(A, B, v0, t0, a.d_model * esz, lds, acc);
+  gemm_tile<T>(A, B, v0, t0, a.d_model * esz, (lds_t*)lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t vbase = v0 + wm * 128;
+  const int wm = wave / kWN, wn = wave % kWN;
+  const int64_t vbase = v0 + wm * (kTile / kWM);
   const float c2 = a.inv_tau * kLog2e;
-  const float gout = a.grad_output ? *a.grad_output : 1.0f;
   const int hi = lane >> 5;
-  const int vlim = (int)((a.v_real - vbase) < 128 ? (a.v_real - vbase) : 128);
+  const int64_t kb = a.v_k * esz;   // bytes of one dz row along K (vocabulary)
+  // (g, lse2) of the lane's token columns; tokens past the chunk read zeros
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gl, (uint32_t)(a.chunk_tokens * 8));
 
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t t = t0 + wn * 128 + j * 32 + (lane & 31);
-    float g = 0.0f, lse2 = 0.0f;
-    int ty = -1;  // target row relative to vbase, if inside this wave's rows
-    if (t < a.chunk_tokens && token_is_active(a.mask, a.y, a.ignore_index, t)) {
-      g = gout * a.coef[t] * a.inv_tau;
-      lse2 = a.lse[t] * kLog2e;
-      const int64_t yy = a.y[t];
-      if (yy >= vbase && yy < vbase + 128) ty = (int)(yy - vbase);
-    }
-    char* rowp = (char*)a.dz + (t * a.v_k) * esz;
+  for (int j = 0; j < kBJ; ++j) {
+    const int64_t t = t0 + wn * (kTile / kWN) + j * 32 + (lane & 31);
+    // (cast the whole vector: clang miscompiles bit_cast of a single vector element)
+    const f32x2 glv = __builtin_bit_cast(
+        f32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, (uint32_t)(t * 8), 0, 0));
+    const float g = glv[0];
+    const float lse2 = glv[1];
+    char* rowp = (char*)a.dz + (t >> 8) * 256 * kb + (t & 255) * 128;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kBI; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int rq = i * 32 + q * 8 + hi * 4;
+        const int64_t v = vbase + i * 32 + q * 8 + hi * 4;   // 4 consecutive vocabulary rows
         float d[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = rq + e;
-          const float p = fast_exp2(acc[i][j][q * 4 + e] * c2 - lse2);
-          const float x = g * ((r == ty ? 1.0f : 0.0f) - p);
-          d[e] = r < vlim ? x : 0.0f;
-        }
-        Store4<T>::run(rowp + (vbase + rq) * esz, d[0], d[1], d[2], d[3]);
+        for (int e = 0; e < 4; ++e) d[e] = -g * fast_exp2(acc[i][j][q * 4 + e] * c2 - lse2);
+        const int64_t vb = v * esz;
+        Store4<T>::run(rowp + (vb >> 7) * (256 * 128) + (vb & 127), d[0], d[1], d[2], d[3]);
       }
   }
 }
@@ -120,24 +137,24 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, a.group_m, tm, tn);
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
-  f32x16 acc[4][4];
+  f32x16 acc[kBI][kBJ];
   zero_acc(acc);
-  gemm_tile<T>(a.A, a.B, m0, n0, a.k_bytes, lds, acc);
+  gemm_tile<T>(a.A, a.B, m0, n0, a.k_bytes, (lds_t*)lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWN, wn = wave % kWN;
   const int hi = lane >> 5;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+  for (int j = 0; j < kBJ; ++j) {
+    const int64_t n = n0 + wn * (kTile / kWN) + j * 32 + (lane & 31);
     if (n >= a.n_limit) continue;
     const bool zero = n >= a.n_zero_from;
     float* rowp = a.out + n * a.ld_out;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kBI; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t m = m0 + wm * 128 + i * 32 + q * 8 + hi * 4;
+        const int64_t m = m0 + wm * (kTile / kWM) + i * 32 + q * 8 + hi * 4;
         if (m >= a.m_limit) continue;
         f32x4 v = {acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
                    acc[i][j][q * 4 + 3]};
@@ -148,24 +165,37 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
   }
 }
 
-// dst[c][r] = src[r][c] for r < rows_valid and c < cols_valid, else 0; 64x64 tiles.
-// dst is [dst_rows][dst_cols] with dst_rows, dst_cols multiples of 64.
+// dst = src^T in K-panel layout: dst row c, K element r  <-  src row r, column c,
+// for r < rows_valid and c < cols_valid, else 0.  src is row-major (pitch src_ld
+// elements) or K-panel (rows of src_kb bytes).  64 x 64 element tiles; dst rows
+// are dst_kb bytes long.
 template <typename E>
-__global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ src,
-                                                        int64_t src_ld, int64_t rows_valid,
-                                                        int64_t cols_valid, E* __restrict__ dst,
-                                                        int64_t dst_ld, int tiles_c) {
+__global__ __launch_bounds__(256) void transpose_panel_kernel(const E* __restrict__ src,
+                                                              int64_t src_ld, int src_panel,
+                                                              int64_t src_kb, int64_t rows_valid,
+                                                              int64_t cols_valid,
+                                                              E* __restrict__ dst, int64_t dst_kb,
+                                                              int tiles_c) {
   __shared__ E tile[64][65];
   const int64_t tc = blockIdx.x % tiles_c;   // tile along src columns (dst rows)
-  const int64_t tr = blockIdx.x / tiles_c;   // tile along src rows (dst columns)
+  const int64_t tr = blockIdx.x / tiles_c;   // tile along src rows (dst K)
   const int64_t r0 = tr * 64, c0 = tc * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int64_t esz = sizeof(E);
   for (int k = ty; k < 64; k += 4) {
     const int64_t r = r0 + k, c = c0 + tx;
-    tile[k][tx] = (r < rows_valid && c < cols_valid) ? src[r * src_ld + c] : E(0);
+    E v = E(0);
+    if (r < rows_valid && c < cols_valid) {
+      v = src_panel ? *(const E*)((const char*)src + k_panel_offset(r, c * esz, src_kb))
+                    : src[r * src_ld + c];
+    }
+    tile[k][tx] = v;
   }
   __syncthreads();
-  for (int k = ty; k < 64; k += 4) dst[(c0 + k) * dst_ld + r0 + tx] = tile[tx][k];
+  for (int k = ty; k < 64; k += 4) {
+    const int64_t c = c0 + k, r = r0 + tx;
+    *(E*)((char*)dst + k_panel_offset(c, r * esz, dst_kb)) = tile[tx][k];
+  }
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, int64_t words) {
@@ -184,12 +214,15 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+// transpose of a [src rows][src cols] matrix into a K-panel [dst_rows][dst_k] one
 template <typename E>
-static void transpose(const void* src, int64_t src_ld, int64_t rows_valid, int64_t cols_valid,
-                      void* dst, int64_t dst_rows, int64_t dst_cols, hipStream_t s) {
-  const int tiles_c = (int)(dst_rows / 64), tiles_r = (int)(dst_cols / 64);
-  hipLaunchKernelGGL(transpose_kernel<E>, dim3((unsigned)(tiles_c * tiles_r)), dim3(256), 0, s,
-                     (const E*)src, src_ld, rows_valid, cols_valid, (E*)dst, dst_cols, tiles_c);
+static void transpose_panel(const void* src, int64_t src_ld, bool src_panel, int64_t src_kb,
+                            int64_t rows_valid, int64_t cols_valid, void* dst, int64_t dst_rows,
+                            int64_t dst_k, hipStream_t s) {
+  const int tiles_c = (int)(dst_rows / 64), tiles_r = (int)(dst_k / 64);
+  hipLaunchKernelGGL(transpose_panel_kernel<E>, dim3((unsigned)(tiles_c * tiles_r)), dim3(256), 0,
+                     s, (const E*)src, src_ld, src_panel ? 1 : 0, src_kb, rows_valid, cols_valid,
+                     (E*)dst, dst_k * (int64_t)sizeof(E), tiles_c);
 }
 
 template <typename T>
@@ -198,10 +231,12 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   const WsLayout& L = *a.L;
   const int64_t esz = sizeof(T);
   const int64_t N = a.n_tokens, D = a.d_model, VK = L.v_k;
+  const int64_t Dp = ceil_div(D, kTile) * kTile;   // panel rows of WT and HT
   char* wt = a.ws + L.wt;
   char* ht = a.ws + L.ht;
   char* dz = a.ws + L.dz;
   char* dzt = a.ws + L.dzt;
+  float2* gl = (float2*)(a.ws + L.gl);
 
   // padded vocabulary rows of dW that no tile reaches
   if (a.v_rows > VK) {
@@ -211,8 +246,8 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   if (N == 0) {
     return launch_fill_zero(a.dW, (size_t)(a.v_rows < VK ? a.v_rows : VK) * D * 4, s);
   }
-  // WT[d][v] = W[v][d] for v < v_real, 0 up to v_k
-  transpose<E>(a.W, D, a.v_real, D, wt, D, VK, s);
+  // WT: rows d (Dp, zero past D), K = vocabulary (zero past v_real)
+  transpose_panel<E>(a.W, D, false, 0, a.v_real, D, wt, Dp, VK, s);
   const StageEvents& ev = *a.marks;
 
   const int tiles_v = (int)L.n_vt;
@@ -223,27 +258,35 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     const int tiles_t = (int)(ncp / kTokenTile);
     ev.mark(5, s);
 
-    DlogitsArgs d{a.W, (const char*)a.H + c0 * D * esz, a.y + c0,
-                  a.mask ? a.mask + c0 : nullptr, a.lse + c0, a.coef + c0, a.grad_output,
-                  nc, D, a.v_real, VK, a.ignore_index, a.inv_tau, dz, a.group_fwd};
+    const uint8_t* cmask = a.mask ? a.mask + c0 : nullptr;
+    hipLaunchKernelGGL(dlogits_prep_kernel, dim3((unsigned)ceil_div(nc, 256)), dim3(256), 0, s,
+                       a.y + c0, cmask, a.ignore_index, a.coef + c0, a.lse + c0, a.grad_output,
+                       a.inv_tau, nc, gl);
+    DlogitsArgs d{a.W, (const char*)a.H + c0 * D * esz, gl, nc, D, a.v_real, VK, a.inv_tau, dz,
+                  a.group_fwd};
     hipLaunchKernelGGL(dlogits_kernel<T>, dim3(tiles_v * tiles_t), dim3(kThreads), 0, s, d,
                        tiles_v, tiles_t);
+    TargetArgs fx{(const char*)a.H + c0 * D * esz, a.W, a.y + c0, cmask, nc, D, a.v_real,
+                  a.ignore_index, a.inv_tau, 1, nullptr, a.lse + c0, a.coef + c0,
+                  a.grad_output, dz, VK};
+    hipError_t e0 = launch_target_logit(sizeof(T) == 2 ? 0 : 1, fx, s);
+    if (e0 != hipSuccess) return e0;
     ev.mark(6, s);
 
     // dH rows of the chunk: M = d (WT rows), N = t (dz rows), K = v
-    ProductArgs ph{Operand{wt, VK * esz, D}, Operand{dz, VK * esz, nc}, VK * esz,
+    ProductArgs ph{k_panel(wt, VK * esz, D), k_panel(dz, VK * esz, nc), VK * esz,
                    a.dH + c0 * D, D, D, nc, INT64_MAX, 0, a.group_dh};
     hipLaunchKernelGGL(product_kernel<T>, dim3(tiles_d * tiles_t), dim3(kThreads), 0, s, ph,
                        tiles_d, tiles_t);
     ev.mark(7, s);
 
-    // transposes for dW: dzT[v][t] and HT[d][t]
-    transpose<E>(dz, VK, nc, VK, dzt, VK, ncp, s);
-    transpose<E>((const char*)a.H + c0 * D * esz, D, nc, D, ht, D, ncp, s);
+    // dzT: rows v, K = t;  HT: rows d, K = t
+    transpose_panel<E>(dz, 0, true, VK * esz, ncp, VK, dzt, VK, ncp, s);
+    transpose_panel<E>((const char*)a.H + c0 * D * esz, D, false, 0, nc, D, ht, Dp, ncp, s);
     ev.mark(8, s);
 
     // dW: M = d (HT rows), N = v (dzT rows), K = t
-    ProductArgs pw{Operand{ht, ncp * esz, D}, Operand{dzt, ncp * esz, VK}, ncp * esz,
+    ProductArgs pw{k_panel(ht, ncp * esz, D), k_panel(dzt, ncp * esz, VK), ncp * esz,
                    a.dW, D, D, (a.v_rows < VK ? a.v_rows : VK), a.v_real, c0 > 0 ? 1 : 0,
                    a.group_dw};
     hipLaunchKernelGGL(product_kernel<T>, dim3(tiles_d * tiles_v), dim3(kThreads), 0, s, pw,

@@ -1,14 +1,19 @@
 // Forward: vocabulary-tile logits -> per-tile (max, sumexp) partials -> merge.
 //
 // Tile-streamed selected-token log-prob (Liger-Kernel PR #1160, Summary): each
-// workgroup computes one 256-vocab x 256-token logit tile on the matrix cores,
-// reduces it to one (max, sumexp) partial per token and captures the target
-// logit when the target falls inside the tile; the [N, V] logits never leave
-// registers.  Padded columns (vocab >= v_real) are -inf before the partial is
-// formed, and the merge folds the partials in ascending tile order starting from
-// the identity (-inf, 0) (RL-Kernel PR #291, commit notes: ShardingSpec,
+// workgroup computes one 256-vocab x 256-token logit tile on the matrix cores
+// and reduces it to one (max, sumexp) partial per token; the [N, V] logits never
+// leave registers.  Padded columns (vocab >= v_real) are -inf before the partial
+// is formed, and the merge folds the partials in ascending tile order starting
+// from the identity (-inf, 0) (RL-Kernel PR #291, commit notes: ShardingSpec,
 // ReductionSpec).  Partials are kept in base-2 units: m2 = max z*log2(e) and
 // s = sum 2^(z*log2(e) - m2), so every exponential is one v_exp_f32.
+//
+// The target logit z[t, y_t] is gathered by target_logit_kernel, one wave per
+// token (a length-D dot product), rather than picked out of the tile: keeping the
+// tile epilogue free of per-lane selects and branches keeps the 256 accumulators
+// in registers.  Only the tile that holds the vocabulary's ragged end runs the
+// masking variant of the tile kernel.
 #include "gemm_tile.hpp"
 #include "launch.hpp"
 
@@ -19,72 +24,64 @@ __device__ __forceinline__ bool token_active(const uint8_t* mask, const int64_t*
   return mask ? (mask[t] != 0) : (y[t] != ignore_index);
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int tiles_m,
-                                                            int tiles_n) {
+// kPartial: this launch covers the last vocabulary tile, whose rows >= v_real are
+// padding (their W rows load as zeros) and must count as -inf.
+template <typename T, bool kPartial>
+__global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int tm_first,
+                                                            int tiles_m, int tiles_n) {
   __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
   __shared__ float2 half_stats[2][kTile];
 
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, a.group_m, tm, tn);
+  tm += tm_first;
   const int64_t v0 = (int64_t)tm * kTile;   // vocabulary rows of this tile
   const int64_t t0 = (int64_t)tn * kTile;   // tokens of this tile
   const int64_t esz = Elem<T>::size;
 
-  Operand A{(const char*)a.W, a.d_model * esz, a.v_real};
-  Operand B{(const char*)a.H, a.d_model * esz, a.n_tokens};
-  f32x16 acc[4][4];
+  const Operand A = row_major(a.W, a.d_model * esz, a.v_real);
+  const Operand B = row_major(a.H, a.d_model * esz, a.n_tokens);
+  f32x16 acc[kBI][kBJ];
   zero_acc(acc);
-  gemm_tile<T>(A, B, v0, t0, a.d_model * esz, lds, acc);
+  gemm_tile<T>(A, B, v0, t0, a.d_model * esz, (lds_t*)lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t vbase = v0 + wm * 128;
+  const int wm = wave / kWN, wn = wave % kWN;
   const float c2 = a.inv_tau * kLog2e;
-  const int hi = lane >> 5;
-  // real vocabulary rows of this wave: [0, vlim) relative to vbase
-  const int vlim = (int)((a.v_real - vbase) < 128 ? (a.v_real - vbase) : 128);
+  if (kPartial) {
+    const int64_t left = a.v_real - (v0 + wm * 128);
+    mask_rows(acc, (int)(left < 0 ? 0 : (left > 128 ? 128 : left)));
+  }
 
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tl = wn * 128 + j * 32 + (lane & 31);
-    const int64_t t = t0 + tl;
-    int ty = -1;  // target row inside this wave's 128 vocabulary rows
-    if (t < a.n_tokens && token_active(a.mask, a.y, a.ignore_index, t)) {
-      const int64_t yy = a.y[t];
-      if (yy >= vbase && yy < vbase + 128 && yy < a.v_real) ty = (int)(yy - vbase);
-    }
-    float m = -INFINITY, zt = 0.0f;
-    bool has = false;
+  for (int j = 0; j < kBJ; ++j) {
+    const int tl = wn * (kTile / kWN) + j * 32 + (lane & 31);
+    float m = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kBI; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = i * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
-        const float z = acc[i][j][e];
-        if (row == ty) { zt = z * a.inv_tau; has = true; }
-        const float z2 = (row < vlim) ? z * c2 : -INFINITY;
-        acc[i][j][e] = z2;
-        m = fmaxf(m, z2);
+        acc[i][j][e] *= c2;          // padded rows stay -inf (c2 > 0)
+        m = fmaxf(m, acc[i][j][e]);
       }
     m = fmaxf(m, __shfl_xor(m, 32));
     float s = 0.0f;
-    if (m != -INFINITY) {
+    if (!kPartial || m != -INFINITY) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kBI; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s += fast_exp2(acc[i][j][e] - m);
     }
     s += __shfl_xor(s, 32);
-    if (has) a.zy[t] = zt;
-    if (hi == 0) half_stats[wm][tl] = make_float2(m, s);
+    // both lane halves hold the same (m, s); both write it
+    half_stats[wm][tl] = make_float2(m, s);
   }
   __syncthreads();
 
   // merge the two 128-row halves (wave rows 0 then 1) and write the tile partial
   const int tl = threadIdx.x;
   const int64_t t = t0 + tl;
-  if (t < a.n_tokens) {
+  if (tl < kTile && t < a.n_tokens) {
     const float2 p0 = half_stats[0][tl], p1 = half_stats[1][tl];
     float M, S;
     if (p1.x == -INFINITY) { M = p0.x; S = p0.y; }
@@ -94,6 +91,59 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int t
       S = p0.y * fast_exp2(p0.x - M) + p1.y * fast_exp2(p1.x - M);
     }
     a.partials[(int64_t)tm * a.n_tokens + t] = make_float2(M, S);
+  }
+}
+
+// One wave per token: z[t, y_t] * inv_tau = inv_tau * sum_d H[t, d] W[y_t, d] for
+// an active token with a target in [0, v_real) (fp32 products and sums; bf16
+// products are exact in fp32).  mode 0 writes it to zy[t]; mode 1 (backward)
+// writes the target element of the dlogits row, g_t (1 - exp(z - lse_t)), over
+// the -g_t p value the tile wrote there.
+template <typename T>
+__global__ __launch_bounds__(256) void target_logit_kernel(TargetArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.n_tokens) return;
+  if (!token_active(a.mask, a.y, a.ignore_index, t)) return;
+  const int64_t yy = a.y[t];
+  if (yy < 0 || yy >= a.v_real) return;
+  constexpr int kPer = 16 / (int)sizeof(T);          // elements per 16-byte chunk
+  const T* h = (const T*)a.H + t * a.d_model;
+  const T* w = (const T*)a.W + yy * a.d_model;
+  float acc = 0.0f;
+  for (int64_t d0 = (int64_t)lane * kPer; d0 < a.d_model; d0 += 64 * kPer) {
+    const i32x4 hv = *(const i32x4*)(h + d0);
+    const i32x4 wv = *(const i32x4*)(w + d0);
+    if (sizeof(T) == 2) {
+      const u32x4 hw = __builtin_bit_cast(u32x4, hv), ww = __builtin_bit_cast(u32x4, wv);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t hu = hw[k], wu = ww[k];
+        acc = fmaf(__builtin_bit_cast(float, hu << 16), __builtin_bit_cast(float, wu << 16), acc);
+        acc = fmaf(__builtin_bit_cast(float, hu & 0xffff0000u),
+                   __builtin_bit_cast(float, wu & 0xffff0000u), acc);
+      }
+    } else {
+      // cast whole vectors: clang miscompiles bit_cast of a single vector element
+      const f32x4 hf = __builtin_bit_cast(f32x4, hv), wf = __builtin_bit_cast(f32x4, wv);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc = fmaf(hf[k], wf[k], acc);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane != 0) return;
+  const float z = acc * a.inv_tau;
+  if (a.mode == 0) {
+    a.zy[t] = z;
+  } else {
+    const float g = a.grad_output ? *a.grad_output * a.coef[t] * a.inv_tau
+                                  : a.coef[t] * a.inv_tau;
+    const float v = g * (1.0f - fast_exp2((z - a.lse[t]) * kLog2e));
+    // dz is in K-panel layout: rows = tokens, K = vocabulary
+    char* p = (char*)a.dz + k_panel_offset(t, yy * (int64_t)sizeof(T), a.v_k * (int64_t)sizeof(T));
+    if (sizeof(T) == 2) *(__bf16*)p = (__bf16)v;
+    else *(float*)p = v;
   }
 }
 
@@ -123,17 +173,32 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   a.logp[t] = lp;
 }
 
+template <typename T>
+static void launch_tiles(const FwdTileArgs& a, int tiles_m, int tiles_n, hipStream_t s) {
+  // every tile but the last is entirely inside the real vocabulary
+  const int full = (a.v_real % kTile == 0) ? tiles_m : tiles_m - 1;
+  if (full > 0)
+    hipLaunchKernelGGL((fwd_tile_kernel<T, false>), dim3(full * tiles_n), dim3(kThreads), 0, s,
+                       a, 0, full, tiles_n);
+  if (full < tiles_m)
+    hipLaunchKernelGGL((fwd_tile_kernel<T, true>), dim3(tiles_n), dim3(kThreads), 0, s, a, full,
+                       1, tiles_n);
+}
+
 hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt, hipStream_t s) {
   const int tiles_m = (int)n_vt;
   const int tiles_n = (int)ceil_div(a.n_tokens, kTokenTile);
-  const int nwg = tiles_m * tiles_n;
-  if (nwg == 0) return hipSuccess;
-  if (dtype == 0)
-    hipLaunchKernelGGL(fwd_tile_kernel<__bf16>, dim3(nwg), dim3(kThreads), 0, s, a, tiles_m,
-                       tiles_n);
-  else
-    hipLaunchKernelGGL(fwd_tile_kernel<float>, dim3(nwg), dim3(kThreads), 0, s, a, tiles_m,
-                       tiles_n);
+  if (tiles_m * tiles_n == 0) return hipSuccess;
+  if (dtype == 0) launch_tiles<__bf16>(a, tiles_m, tiles_n, s);
+  else launch_tiles<float>(a, tiles_m, tiles_n, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_target_logit(int dtype, const TargetArgs& a, hipStream_t s) {
+  if (a.n_tokens == 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(a.n_tokens, 4));
+  if (dtype == 0) hipLaunchKernelGGL(target_logit_kernel<__bf16>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(target_logit_kernel<float>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

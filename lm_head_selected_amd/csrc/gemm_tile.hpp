@@ -5,20 +5,31 @@
 // (token rows, hidden contiguous), and the layout the backward's staging buffers
 // are written in.  Accumulation is fp32.
 //
-//  * 256 threads = 4 waves in a 2x2 grid; each wave owns a 128x128 sub-tile as
-//    4x4 blocks of 32x32 MFMA accumulators (256 fp32 per lane).
+//  * 512 threads = 8 waves in a 2 (M) x 4 (N) grid; each wave owns a 128x64
+//    sub-tile as 4x2 blocks of 32x32 MFMA accumulators (128 fp32 per lane), so
+//    two waves share each SIMD and the hardware issues one wave's MFMAs while the
+//    other waits on memory or a barrier.
 //  * K advances 128 bytes per stage (64 bf16 or 32 fp32); one stage of A and B is
 //    2 x 32 KB of LDS, double buffered (128 KB of the CU's 160 KB).
-//  * Global -> LDS through raw buffer loads.  Rows at or beyond the operand's
-//    valid row count fall outside the buffer resource and load as zeros, which
-//    also keeps padded vocabulary rows from ever being read.
+//  * Operands are either row-major (the caller's W and H: rows ld_bytes apart,
+//    a stage 128 bytes further along the row) or K-panel (the backward's own
+//    staging buffers: each 256-row tile stores its K stages one after another,
+//    256 x 128 contiguous bytes per stage), which keeps every stage of a tile in
+//    one small address range.
+//  * Global -> LDS through direct-to-LDS raw buffer loads (no register staging).
+//    Rows at or beyond the operand's valid row count fall outside the buffer
+//    resource and load as zeros, which also keeps padded vocabulary rows from ever
+//    being read.
 //  * LDS rows are 128 B (8 chunks of 16 B); chunk c of row r is stored at chunk
-//    c ^ (r & 7), so both the 16-B writes and the 16-B MFMA fragment reads hit
-//    all 32 banks once per 8 lanes.
+//    c ^ ((r >> 1) & 7).  gfx950's LDS has 64 banks (256 B) and serves a 16-byte
+//    read for 16 lanes per pass; a fragment read has 16 lanes on 16 consecutive
+//    rows at one logical chunk, i.e. physical (r & 1, c ^ ((r >> 1) & 7)), all
+//    distinct, so every pass touches each bank once.
 //  * bf16: v_mfma_f32_32x32x16_bf16, one per 16-B fragment pair.  fp32:
 //    v_mfma_f32_32x32x2_f32, four per fragment pair (exact fp32 products).
 //
-// Accumulator layout (per wave, block (i, j), element e of the 16):
+// Accumulator layout (per wave, block (i, j), element e of the 16), relative to
+// the wave's sub-tile at (wm * 128, wn * 64):
 //   row (M) = i*32 + (e >> 2)*8 + (lane >> 5)*4 + (e & 3)
 //   col (N) = j*32 + (lane & 31)
 // so each lane holds 4 consecutive M indices for one N index per (i, j, e>>2).
@@ -29,16 +40,38 @@
 namespace gh {
 
 constexpr int kTile = 256;
-constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;                     // K bytes per stage per row
-constexpr int kStageBytes = 2 * kTile * kRowBytes; // A + B
-constexpr int kGemmLds = 2 * kStageBytes;          // double buffered
+constexpr int kWM = 2, kWN = 4;                 // wave grid
+constexpr int kWaves = kWM * kWN;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBI = kTile / kWM / 32;           // 32-row accumulator blocks per wave (M)
+constexpr int kBJ = kTile / kWN / 32;           // 32-col accumulator blocks per wave (N)
+// K pipeline: 128-byte K stages, 2 LDS buffers (128 KB)
+constexpr int kRowB = 128;
+constexpr int kNst = 2;
 
+// Addressing of an operand: byte (row r of tile t, stage s, chunk c) lives at
+//   base + t * tile_bytes + (r % 256) * ld_bytes + s * stage_bytes + 16 c.
 struct Operand {
-  const char* base;   // element (0, 0)
-  int64_t ld_bytes;   // bytes between rows (multiple of 16)
-  int64_t rows;       // valid rows; rows beyond load as zero
+  const char* base;     // element (0, 0)
+  int64_t ld_bytes;     // bytes between rows of a tile (row-major: the row pitch)
+  int64_t stage_bytes;  // bytes between K stages (row-major: 128)
+  int64_t tile_bytes;   // bytes between 256-row tiles (row-major: 256 * pitch)
+  int64_t rows;         // valid rows; row-major rows beyond load as zero
+  bool panel;           // K-panel layout: every row of every tile is initialised
 };
+
+__host__ __device__ inline Operand row_major(const void* base, int64_t pitch, int64_t rows) {
+  return Operand{(const char*)base, pitch, 128, 256 * pitch, rows, false};
+}
+// K-panel layout of a [rows_pad][k_bytes] matrix (rows_pad a multiple of 256)
+__host__ __device__ inline Operand k_panel(const void* base, int64_t k_bytes, int64_t rows) {
+  return Operand{(const char*)base, 128, 256 * 128, 256 * k_bytes, rows, true};
+}
+// Byte offset of (row, byte kb along K) in the K-panel layout of a matrix whose
+// rows hold k_bytes.
+__host__ __device__ inline int64_t k_panel_offset(int64_t row, int64_t kb, int64_t k_bytes) {
+  return (row >> 8) * 256 * k_bytes + (kb >> 7) * (256 * 128) + (row & 255) * 128 + (kb & 127);
+}
 
 template <typename T> struct Mma;
 template <> struct Mma<__bf16> {
@@ -58,93 +91,184 @@ template <> struct Mma<float> {
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const Operand& op, int64_t r0) {
+  const char* base = op.base + (r0 >> 8) * op.tile_bytes;
+  if (op.panel) return make_rsrc(base, (uint32_t)op.tile_bytes);
   int64_t valid = op.rows - r0;
   valid = valid < 0 ? 0 : (valid > kTile ? kTile : valid);
-  return make_rsrc(op.base + r0 * op.ld_bytes, (uint32_t)(valid * op.ld_bytes));
+  return make_rsrc(base, (uint32_t)(valid * op.ld_bytes));
 }
 
+typedef __attribute__((address_space(3))) char lds_t;
+
+__device__ __forceinline__ i32x4 lds_read16(const lds_t* p) {
+  return *(const __attribute__((address_space(3))) i32x4*)p;
+}
+
+template <int N> __device__ __forceinline__ void wait_vm() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for the K pipeline.  __syncthreads() would also drain every
+// in-flight direct-to-LDS load (its fence waits for vmcnt(0)); here the caller
+// waits for exactly the stage it needs, and this wave's LDS reads are drained
+// so no other wave's loads can overwrite a buffer still being read.
+__device__ __forceinline__ void pipe_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Shape of the K pipeline: ROWB bytes of K per stage and row (64 or 128) and
+// NST stage buffers in LDS (loads run NST - 1 stages ahead of the MFMAs).
+template <int ROWB, int NST> struct Pipe {
+  static_assert(ROWB == 64 || ROWB == 128, "stage row bytes");
+  static_assert(NST >= 2 && NST <= 5, "stages");
+  static constexpr int kChunks = ROWB / 16;             // 16-byte chunks per row
+  static constexpr int kStage = 2 * kTile * ROWB;       // A + B bytes per stage
+  static constexpr int kLds = NST * kStage;
+  static constexpr int kRowsPerLoad = 1024 / ROWB;      // rows one wave-wide load covers
+  static constexpr int kKs = ROWB / 32;                 // 16-element bf16 K sub-steps
+  // physical chunk of logical chunk c in row r; 16 consecutive rows read at one
+  // logical chunk land on 16 distinct 16-byte bank groups of the 64-bank LDS
+  static __device__ __forceinline__ int swz(int r) {
+    return ROWB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+  }
+};
+
+// LDS bytes of the default pipeline.
+constexpr int kGemmLds = Pipe<kRowB, kNst>::kLds;
+
 // acc[i][j] += A[m0 + wave rows] . B[n0 + wave cols]^T over k_bytes of K.
-template <typename T>
+//
+// Stage s (ROWB bytes of K) lives in LDS buffer s % NST.  Each wave fills its
+// share of a stage with direct-to-LDS buffer loads (16 B per lane; lane l's
+// bytes land at the block base + 16 l, so the lane fetches the logical chunk
+// that belongs at that physical position of the swizzled row).  Iteration s:
+//   issue the loads of stage s + NST - 1 (into the buffer stage s - 1 used);
+//   for each 16-element sub-step: read the next fragments, run 16 MFMAs on the
+//   current ones; before the last sub-step's MFMAs, wait for stage s + 1's loads,
+//   barrier, and read stage s + 1's first fragments, so that LDS latency hides
+//   under those MFMAs.
+// The loop has no data-dependent branches: stages past the end of K are loaded
+// and read like the others (their offsets stay inside the operand, or past the
+// resource end where loads return zeros) and are never used, so every wait count
+// is a constant.  All loads are drained before returning: none may write LDS
+// after the workgroup releases it.
+template <typename T, int ROWB = kRowB, int NST = kNst>
 __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, int64_t m0,
-                                          int64_t n0, int64_t k_bytes, char* lds,
-                                          f32x16 (&acc)[4][4]) {
+                                          int64_t n0, int64_t k_bytes, lds_t* lds,
+                                          f32x16 (&acc)[kBI][kBJ]) {
+  typedef Pipe<ROWB, NST> P;
+  static_assert(ROWB == 128, "operand stage strides assume 128-byte stages");
+  constexpr int kLoads = kTile / P::kRowsPerLoad / kWaves;   // per wave per operand
+  constexpr int kAhead = (NST - 2) * 2 * kLoads;              // loads allowed in flight
+  static_assert(kAhead <= 63, "vmcnt range");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWN, wn = wave % kWN;
 
   const __amdgpu_buffer_rsrc_t ra = tile_rsrc(A, m0);
   const __amdgpu_buffer_rsrc_t rb = tile_rsrc(B, n0);
 
-  // global loads: thread covers rows (tid >> 3) + 32 i, chunk (tid & 7)
-  const int lrow = tid >> 3, lchunk = tid & 7;
-  const uint32_t goffA = (uint32_t)(lrow * A.ld_bytes + lchunk * 16);
-  const uint32_t goffB = (uint32_t)(lrow * B.ld_bytes + lchunk * 16);
-  const uint32_t gstepA = (uint32_t)(32 * A.ld_bytes), gstepB = (uint32_t)(32 * B.ld_bytes);
-  const int swz_w = ((lchunk ^ (lrow & 7)) << 4);
-  const int lds_w = lrow * kRowBytes + swz_w;    // + i * 32 * kRowBytes
+  // direct loads: wave-wide load i covers tile rows (wave + kWaves i) * 8 + lane / 8
+  const int lrow = wave * P::kRowsPerLoad + lane / P::kChunks;
+  const uint32_t cswz = (uint32_t)(((lane % P::kChunks) ^ P::swz(lrow)) << 4);
+  const uint32_t offA = (uint32_t)(lrow * A.ld_bytes) + cswz;
+  const uint32_t offB = (uint32_t)(lrow * B.ld_bytes) + cswz;
+  const uint32_t stepA = (uint32_t)(kWaves * P::kRowsPerLoad * A.ld_bytes);
+  const uint32_t stepB = (uint32_t)(kWaves * P::kRowsPerLoad * B.ld_bytes);
+  const uint32_t kstA = (uint32_t)A.stage_bytes, kstB = (uint32_t)B.stage_bytes;
 
-  // fragment reads: row (w*128 + i*32 + (lane & 31)), chunk 2s + (lane >> 5)
+  // fragment reads: row (wave origin + 32 i + (lane & 31)), logical chunk 2 ks + (lane >> 5)
   const int frow = lane & 31, fhalf = lane >> 5;
-  const int fA = (wm * 128 + frow) * kRowBytes;
-  const int fB = kTile * kRowBytes + (wn * 128 + frow) * kRowBytes;
-  int fswz[4];
+  const int fA = (wm * (kTile / kWM) + frow) * ROWB;
+  const int fB = kTile * ROWB + (wn * (kTile / kWN) + frow) * ROWB;
+  int fswz[P::kKs];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) fswz[s] = (((2 * s + fhalf) ^ (frow & 7)) << 4);
+  for (int ks = 0; ks < P::kKs; ++ks) fswz[ks] = (((2 * ks + fhalf) ^ P::swz(frow)) << 4);
 
-  const int nk = (int)(k_bytes / kRowBytes);
-  i32x4 pa[8], pb[8];
+  const int nk = (int)(k_bytes / ROWB);
 
-  auto gload = [&](int kt) {
-    const uint32_t soff = (uint32_t)kt * kRowBytes;
+  auto issue = [&](int stage) {
+    lds_t* sa = lds + (stage % NST) * P::kStage + wave * 1024;
+    lds_t* sb = sa + kTile * ROWB;
+    const uint32_t ka = (uint32_t)stage * kstA, kb = (uint32_t)stage * kstB;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pa[i] = buffer_load16(ra, goffA + i * gstepA, soff);
-      pb[i] = buffer_load16(rb, goffB + i * gstepB, soff);
+    for (int i = 0; i < kLoads; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + i * kWaves * 1024, 16,
+                                               offA + i * stepA + ka, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + i * kWaves * 1024, 16,
+                                               offB + i * stepB + kb, 0, 0, 0);
     }
   };
-  auto lstore = [&](int stage) {
-    char* s = lds + stage * kStageBytes;
+  auto read_frags = [&](i32x4 (&fa)[kBI], i32x4 (&fb)[kBJ], int stage, int ks) {
+    const lds_t* s = lds + (stage % NST) * P::kStage;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *(i32x4*)(s + lds_w + i * 32 * kRowBytes) = pa[i];
-      *(i32x4*)(s + kTile * kRowBytes + lds_w + i * 32 * kRowBytes) = pb[i];
-    }
+    for (int i = 0; i < kBI; ++i) fa[i] = lds_read16(s + fA + i * 32 * ROWB + fswz[ks]);
+#pragma unroll
+    for (int j = 0; j < kBJ; ++j) fb[j] = lds_read16(s + fB + j * 32 * ROWB + fswz[ks]);
   };
-  auto compute = [&](int stage) {
-    const char* s = lds + stage * kStageBytes;
+  auto mma = [&](const i32x4 (&fa)[kBI], const i32x4 (&fb)[kBJ]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      i32x4 fa[4], fb[4];
+    for (int i = 0; i < kBI; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = *(const i32x4*)(s + fA + i * 32 * kRowBytes + fswz[ks]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = *(const i32x4*)(s + fB + j * 32 * kRowBytes + fswz[ks]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Mma<T>::run(acc[i][j], fa[i], fb[j]);
-    }
+      for (int j = 0; j < kBJ; ++j) Mma<T>::run(acc[i][j], fa[i], fb[j]);
   };
 
   if (nk <= 0) return;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  i32x4 fa0[kBI], fb0[kBJ], fa1[kBI], fb1[kBJ];
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue(s);
+  wait_vm<kAhead>();
+  pipe_barrier();
+  read_frags(fa0, fb0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // sched_barrier(0) pins each phase: the next fragments' LDS reads are issued
+  // before the MFMAs that consume the current ones.
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    compute(cur);
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+    issue(kt + NST - 1);
+#pragma unroll
+    for (int ks = 0; ks < P::kKs; ++ks) {
+      i32x4(&cur_a)[kBI] = (ks & 1) ? fa1 : fa0;
+      i32x4(&cur_b)[kBJ] = (ks & 1) ? fb1 : fb0;
+      i32x4(&nxt_a)[kBI] = (ks & 1) ? fa0 : fa1;
+      i32x4(&nxt_b)[kBJ] = (ks & 1) ? fb0 : fb1;
+      if (ks + 1 < P::kKs) {
+        read_frags(nxt_a, nxt_b, kt, ks + 1);
+      } else {
+        wait_vm<kAhead>();
+        pipe_barrier();
+        read_frags(nxt_a, nxt_b, kt + 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma(cur_a, cur_b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  wait_vm<0>();
+  pipe_barrier();
 }
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
+// Set every accumulator whose wave-local M row (0..127) is >= vlim to -inf.
+// Used once per tile, only on the tile holding the vocabulary's ragged end;
+// each row mask serves the four column blocks and dies.
+__device__ __forceinline__ void mask_rows(f32x16 (&acc)[kBI][kBJ], int vlim) {
+  const int hi = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int e = 0; e < 16; ++e) {
+      const bool pad = i * 32 + (e >> 2) * 8 + hi * 4 + (e & 3) >= vlim;
+#pragma unroll
+      for (int j = 0; j < kBJ; ++j) acc[i][j][e] = pad ? -INFINITY : acc[i][j][e];
+    }
+}
+
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[kBI][kBJ]) {
+#pragma unroll
+  for (int i = 0; i < kBI; ++i)
+#pragma unroll
+    for (int j = 0; j < kBJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 }

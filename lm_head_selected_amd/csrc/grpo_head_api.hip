@@ -111,8 +111,10 @@ gh::WsLayout layout(const grpo_head_params* p, bool with_gemm = true) {
   L.chunk = chunk;
   off = 0;
   L.bflags = take(64);
-  L.wt = take((size_t)D * L.v_k * esz);
-  L.ht = take((size_t)D * chunk * esz);
+  L.gl = take((size_t)chunk * 8);
+  const int64_t Dp = gh::ceil_div(D, 256) * 256;   // panel rows of W^T and H^T
+  L.wt = take((size_t)Dp * L.v_k * esz);
+  L.ht = take((size_t)Dp * chunk * esz);
   L.dz = take((size_t)chunk * L.v_k * esz);
   L.dzt = take((size_t)L.v_k * chunk * esz);
   L.bwd_bytes = off > L.fwd_bytes ? off : L.fwd_bytes;
@@ -226,11 +228,15 @@ int grpo_head_fwd(const grpo_head_params* p, const void* H, const void* W, const
   hipError_t e;
   if (p->n_tokens > 0) {
     g_marks.mark(0, s);
-    gh::FwdTileArgs fa{W, H, y, mask, p->n_tokens, p->d_model, p->v_real, p->ignore_index,
-                       p->inv_tau, (float2*)(w + L.partials), (float*)(w + L.zy), kGroupFwd};
+    gh::FwdTileArgs fa{W, H, p->n_tokens, p->d_model, p->v_real, p->inv_tau,
+                       (float2*)(w + L.partials), kGroupFwd};
     e = gh::launch_fwd_tiles(p->dtype, fa, L.n_vt, s);
     if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
     g_marks.mark(1, s);
+    gh::TargetArgs ta{H, W, y, mask, p->n_tokens, p->d_model, p->v_real, p->ignore_index,
+                      p->inv_tau, 0, (float*)(w + L.zy), nullptr, nullptr, nullptr, nullptr, 0};
+    e = gh::launch_target_logit(p->dtype, ta, s);
+    if (e != hipSuccess) return hip_fail(e, "target logit kernel");
     gh::MergeArgs ma{(const float2*)(w + L.partials), (const float*)(w + L.zy), y, mask,
                      p->n_tokens, L.n_vt, p->v_real, p->ignore_index, logp, lse};
     e = gh::launch_merge(ma, s);

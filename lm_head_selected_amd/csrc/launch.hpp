@@ -20,7 +20,7 @@ struct WsLayout {
   size_t partials = 0, zy = 0, seq_L = 0, seq_F = 0, seq_G = 0, scal = 0, flags = 0;
   size_t fwd_bytes = 0;
   // backward (reuses the workspace from offset 0)
-  size_t bflags = 0, wt = 0, ht = 0, dz = 0, dzt = 0;
+  size_t bflags = 0, gl = 0, wt = 0, ht = 0, dz = 0, dzt = 0;
   size_t bwd_bytes = 0;
   int64_t n_vt = 0;        // vocabulary tiles covering [0, v_real)
   int64_t v_k = 0;         // n_vt * 256: vocabulary extent of the staging buffers
@@ -31,12 +31,22 @@ struct WsLayout {
 enum : uint32_t { kFlagTarget = 1u, kFlagNonfinite = 2u, kFlagSid = 4u };
 
 struct FwdTileArgs {
-  const void* W; const void* H; const int64_t* y; const uint8_t* mask;
-  int64_t n_tokens, d_model, v_real, ignore_index;
+  const void* W; const void* H;
+  int64_t n_tokens, d_model, v_real;
   float inv_tau;
   float2* partials;  // [n_vt][n_tokens]
-  float* zy;         // [n_tokens]
   int group_m;
+};
+// Target-logit gather (mode 0: zy[t]) or the backward's target-element fix-up
+// (mode 1: dz[t][y_t] = g_t (1 - p_t,y)); pointers already offset to the chunk.
+struct TargetArgs {
+  const void* H; const void* W; const int64_t* y; const uint8_t* mask;
+  int64_t n_tokens, d_model, v_real, ignore_index;
+  float inv_tau;
+  int mode;
+  float* zy;
+  const float* lse; const float* coef; const float* grad_output;
+  void* dz; int64_t v_k;
 };
 struct MergeArgs {
   const float2* partials; const float* zy; const int64_t* y; const uint8_t* mask;
@@ -80,6 +90,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt, hipStream_t s);
+hipError_t launch_target_logit(int dtype, const TargetArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_loss(const LossArgs& a, hipStream_t s);
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
