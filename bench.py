@@ -2,16 +2,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--cpu-tokens T | --no-cpu-baseline]
+    python bench.py --copy-calibration      # plain 1 GiB copies, for HBM counters
 
 One step is one pass of the whole hot path over one batch: selected-token
-log-prob over vocabulary tiles, fixed-order merge, GRPO objective, recomputed
-dlogits, dH and dW.  Inputs are synthetic and resident in HBM before timing
-starts; old/reference log-probs are this policy's own log-probs plus seeded
-noise.  Prints one JSON line.
+log-prob over vocabulary tiles, fixed-order merge, GRPO (or GSPO) objective,
+recomputed dlogits, dH and dW.  Inputs are synthetic and resident in HBM before
+timing starts.  The old / reference log-probs are the fp64 CPU reference's
+policy log-probs stored with the tests (tests/golden) plus the workload's seeded
+noise, so no input is derived from the GPU's own results.  Prints one JSON line.
 """
 import argparse
+import hashlib
+import glob
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -21,7 +26,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
-PEAK_HBM_GBS = 8000.0
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+COPY_BYTES = 1 << 30
 
 
 def parse():
@@ -30,9 +36,51 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_8b_head_grpo_n8192")
-    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=3072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
+
+
+def source_digest() -> str:
+    """sha256 over the HIP sources and the C header: identifies the kernels that
+    a stored counter measurement belongs to."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "lm_head_selected_amd", "csrc", "*")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, kernel_stage: str):
+    """HBM bytes per launch of the given stage's kernel from the committed counter
+    summary (FETCH_SIZE / WRITE_SIZE, copy-calibrated), or None when there is no
+    summary or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel_stage)
+    if k is None:
+        return None
+    return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def policy_logp(workload: str):
+    """The fp64 CPU reference's selected-token log-probs for this workload, as
+    stored by tests/golden/make_fullsize.py."""
+    path = os.path.join(ROOT, "tests", "golden", f"fullsize_{workload}.npz")
+    if not os.path.exists(path):
+        raise SystemExit(f"no stored policy log-probs for workload {workload!r} ({path}); "
+                         "the benchmark runs the full-size workloads only")
+    with np.load(path) as z:
+        return np.asarray(z["logp"], dtype=np.float64)
 
 
 def device_inputs(inp, dev, torch):
@@ -44,12 +92,13 @@ def device_inputs(inp, dev, torch):
     else:
         H, W = t(inp["H"], torch.float32), t(inp["W"], torch.float32)
     return dict(H=H, W=W, y=t(inp["y"], torch.int64), mask=t(inp["mask"], torch.uint8),
-                sid=t(inp["sid"], torch.int32), adv=t(inp["adv"], torch.float32))
+                sid=t(inp["sid"], torch.int32), adv=t(inp["adv"], torch.float32),
+                old=t(inp["old_logp"], torch.float32), ref=t(inp["ref_logp"], torch.float32))
 
 
 class HipEvents:
     """Raw hipEvent_t handles from the HIP runtime torch already loaded (same
-    soname), for events the library records on its stream."""
+    soname), for events the library records on its own launch stream."""
 
     def __init__(self):
         import ctypes
@@ -79,49 +128,70 @@ class HipEvents:
         self.made = []
 
 
-def cpu_baseline(inp, old, ref, n_tok):
+def cpu_baseline(inp, n_tok):
     """The fp64 oracle, as it stands, on the first n_tok tokens of the workload
     (treated as their own batch): forward, objective, backward."""
     import oracle
     from threadpoolctl import threadpool_info
     s = min(n_tok, inp["n_tokens"])
     y, mask, sid = inp["y"][:s], None if inp["mask"] is None else inp["mask"][:s], inp["sid"][:s]
+    old = inp["old_logp"][:s]
+    ref = None if inp["ref_logp"] is None else inp["ref_logp"][:s]
     t0 = time.perf_counter()
     act = oracle.active_tokens(y, mask, inp["ignore_index"])
     lp, lse = oracle.forward(inp["H"][:s], inp["W"], y, act, inp["v_real"], inp["inv_tau"],
                              inp["dtype"], block=256)
     n_s = int(sid.max()) + 1
     if inp["level"] == "sequence_gspo":
-        obj = oracle.gspo_objective(lp, old[:s], None if ref is None else ref[:s], inp["adv"][:n_s],
-                                    sid, act, n_s, inp["eps_low"], inp["eps_high"], inp["beta"])
+        obj = oracle.gspo_objective(lp, old, ref, inp["adv"][:n_s], sid, act, n_s,
+                                    inp["eps_low"], inp["eps_high"], inp["beta"])
     else:
-        obj = oracle.grpo_objective(lp, old[:s], None if ref is None else ref[:s], inp["adv"][:n_s],
-                                    sid, act, n_s, inp["eps_low"], inp["eps_high"], inp["beta"],
+        obj = oracle.grpo_objective(lp, old, ref, inp["adv"][:n_s], sid, act, n_s,
+                                    inp["eps_low"], inp["eps_high"], inp["beta"],
                                     inp["reduction"])
     oracle.backward(inp["H"][:s], inp["W"], y, act, lse, obj["coef"], inp["v_real"],
                     inp["inv_tau"], 1.0, inp["dtype"], block=256)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()
                    if p.get("user_api") == "blas"] or [1])
-    return {"value": s / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {s} tokens of the same workload as one batch, fp64 forward + "
-                      f"objective + backward in {dt:.1f} s"}
+    return {"value": round(s / dt, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {s} of {inp['n_tokens']} tokens of the same workload as one batch "
+                      f"(full D and V): fp64 forward + objective + backward, {dt:.1f} s"}
+
+
+def copy_calibration():
+    """Three launches of one elementwise kernel that reads COPY_BYTES and writes
+    COPY_BYTES (b = -a over fp32), for scaling the HBM byte counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": COPY_BYTES,
+                      "copy_calibration_bytes_written": COPY_BYTES, "launches": 3}), flush=True)
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: this build "
-              "has no multi-GPU path (the sharding plan is described in DESIGN.md)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library "
+              "runs on a single GPU (the multi-GPU sharding plan is design-only)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     from lm_head_selected_amd import binding as gb
-    from synth import config, make_inputs
+    from synth import attach_logprobs, config, make_inputs
 
     cfg = config(args.workload)
     dev = torch.device("cuda:0")
-    inp = make_inputs(cfg)
+    inp = attach_logprobs(make_inputs(cfg), policy_logp(cfg.name))
     d = device_inputs(inp, dev, torch)
     N, D, V = cfg.n_tokens, cfg.d_model, cfg.v_real
     p = gb.make_params(n_tokens=N, d_model=D, v_real=V, v_rows=cfg.v_rows, n_seqs=inp["n_seqs"],
@@ -129,22 +199,14 @@ def main():
                        inv_tau=cfg.inv_tau, eps_low=cfg.eps_low, eps_high=cfg.eps_high,
                        beta=cfg.beta)
     head = gb.GrpoHead(p, dev)
-
-    # old/ref = this policy's log-prob + seeded noise (the forward is the product path)
-    zeros = torch.zeros(N, device=dev)
-    head.fwd(d["H"], d["W"], d["y"], d["mask"], d["sid"], d["adv"], zeros,
-             zeros if cfg.beta > 0 else None)
-    torch.cuda.synchronize()
-    base = head.logp.double()
-    nz = lambda a: None if a is None else torch.from_numpy(a).to(dev)  # noqa: E731
-    old = (base + nz(inp["noise_old"])).float()
-    ref = None if inp["noise_ref"] is None else (base + nz(inp["noise_ref"])).float()
     dH = torch.empty(N, D, dtype=torch.float32, device=dev)
     dW = torch.empty(cfg.v_rows, D, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
 
     def step():
-        head.fwd(d["H"], d["W"], d["y"], d["mask"], d["sid"], d["adv"], old, ref)
-        head.bwd(d["H"], d["W"], d["y"], d["mask"], dH=dH, dW=dW)
+        head.fwd(d["H"], d["W"], d["y"], d["mask"], d["sid"], d["adv"], d["old"], d["ref"],
+                 stream=stream)
+        head.bwd(d["H"], d["W"], d["y"], d["mask"], dH=dH, dW=dW, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -152,52 +214,63 @@ def main():
 
     K = args.steps
     hev = HipEvents()
-    evs = [[hev.create() for _ in range(10)] for _ in range(K)]
+    evs = [[hev.create() for _ in range(gb.N_STAGE_EVENTS)] for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
+    start.record(stream)
     for k in range(K):
         gb.set_stage_events(evs[k])
         step()
-    end.record()
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gb.set_stage_events(None)
     ms_step = start.elapsed_time(end) / K
-    value = N * K / (ms_step * K / 1e3)
+    value = N / (ms_step / 1e3)
 
-    flops_gemm = 2.0 * N * V * D
     stages = {}
     for name, (a, b) in gb.STAGES.items():
         stages[name] = float(np.mean([hev.elapsed_ms(evs[k][a], evs[k][b]) for k in range(K)]))
+    per_step = [hev.elapsed_ms(evs[k][0], evs[k][gb.N_STAGE_EVENTS - 1]) for k in range(K)]
     hev.destroy()
-    gemm_stages = ("fwd_tiles", "bwd_dlogits", "bwd_dh", "bwd_dw")
-    dom = max(gemm_stages, key=lambda s: stages[s])
-    achieved = flops_gemm / (stages[dom] / 1e3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
 
+    # algorithmic flops of each matrix-core launch: 2 N D x (real vocabulary rows it covers)
+    full_rows = (V // 256) * 256 if V % 256 else V
+    launch_flops = {"fwd_tiles": 2.0 * N * D * full_rows, "bwd_dlogits": 2.0 * N * D * V,
+                    "bwd_dh": 2.0 * N * D * V, "bwd_dw": 2.0 * N * D * V}
+    gemm = {s: {"ms": round(stages[s], 3),
+                "tflops": round(launch_flops[s] / (stages[s] / 1e3) / 1e12, 1)}
+            for s in gb.GEMM_STAGES}
+    dom = max(gb.GEMM_STAGES, key=lambda s: stages[s])
+    achieved = launch_flops[dom] / (stages[dom] / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic(cfg.name, dom),
+                "kernel": gb.GEMM_STAGES[dom], "stage": dom,
+                "flops_per_launch": launch_flops[dom], "launch_ms": round(stages[dom], 3)}
+
+    flops_8nvd = 8.0 * N * V * D
     out = {
         "metric": "tokens/s fwd+bwd fused GRPO head loss + % bf16 MFMA peak, D=4096 V=151936",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": N, "d_model": D, "v_real": V,
                    "v_rows": cfg.v_rows, "sequences": int(inp["n_seqs"]),
                    "reduction": cfg.reduction, "level": cfg.level, "parallelism": "none"},
-        "tflops_8nvd": round(4 * flops_gemm / (ms_step / 1e3) / 1e12, 1),
-        "tflops_6nvd": round(3 * flops_gemm / (ms_step / 1e3) / 1e12, 1),
-        "frac_of_peak_8nvd": round(4 * flops_gemm / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "step_ms_median": round(statistics.median(per_step), 3),
+        "step_ms_min": round(min(per_step), 3),
+        "tflops_8nvd": round(flops_8nvd / (ms_step / 1e3) / 1e12, 1),
+        "tflops_6nvd": round(0.75 * flops_8nvd / (ms_step / 1e3) / 1e12, 1),
+        "frac_of_peak_8nvd": round(flops_8nvd / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "gemm_launches": gemm,
         "stages_ms": {k: round(v, 3) for k, v in stages.items()},
         "wall_s": round(wall, 3),
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, old.cpu().numpy(),
-                                           None if ref is None else ref.cpu().numpy(),
-                                           args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
     print(json.dumps(out), flush=True)
 
 

@@ -207,14 +207,16 @@ size_t gspo_segment_workspace_size(const grpo_head_params* p);
  * hipEvent_t handles (cast to void*; NULL entries are skipped), or events == NULL
  * to switch timing off.  The array is copied.  While set, the calls record
  * events on their stream at stage boundaries:
- *   grpo_head_fwd: [0] before the tile kernels, [1] after them, [2] after the
- *                  target-logit gather and the merge, [3] after the objective
- *                  stage;
- *   grpo_head_bwd: [4] at entry, [5] at each token chunk's start (after the
- *                  transpose of W for the first chunk), [6] after the dlogits
- *                  kernels, [7] after the dH product, [8] after the two
- *                  transposes, [9] after the dW product (with several chunks,
- *                  [5]-[9] describe the last one).
+ *   grpo_head_fwd: [0] before the launch of the full vocabulary tiles, [1] after
+ *                  it, [2] after the ragged-end tile, the target-logit gather
+ *                  and the merge, [3] after the objective stage;
+ *   grpo_head_bwd: [4] at entry, [5] just before a token chunk's dlogits tile
+ *                  launch (after the transpose of W and the per-token prep),
+ *                  [6] after that launch, [7] after the target-element fix-up,
+ *                  [8] after the dH product, [9] after the two transposes,
+ *                  [10] after the dW product (with several chunks, [5]-[10]
+ *                  describe the last one).
+ * So [0]-[1], [5]-[6], [7]-[8] and [9]-[10] each bracket one matrix-core launch.
  * Returns GRPO_HEAD_INVALID_ARGUMENT if n_events < 0 or > 16. */
 int grpo_head_set_stage_events(void* const* events, int n_events);
 

@@ -130,7 +130,8 @@ struct ProductArgs {
   int group_m;
 };
 
-template <typename T>
+// kRole only separates the dH (0) and dW (1) launches under a profiler.
+template <typename T, int kRole>
 __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int tiles_m,
                                                            int tiles_n) {
   __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
@@ -256,7 +257,6 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     const int64_t nc = (N - c0) < L.chunk ? (N - c0) : L.chunk;
     const int64_t ncp = ceil_div(nc, kTokenTile) * kTokenTile;
     const int tiles_t = (int)(ncp / kTokenTile);
-    ev.mark(5, s);
 
     const uint8_t* cmask = a.mask ? a.mask + c0 : nullptr;
     hipLaunchKernelGGL(dlogits_prep_kernel, dim3((unsigned)ceil_div(nc, 256)), dim3(256), 0, s,
@@ -264,34 +264,36 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
                        a.inv_tau, nc, gl);
     DlogitsArgs d{a.W, (const char*)a.H + c0 * D * esz, gl, nc, D, a.v_real, VK, a.inv_tau, dz,
                   a.group_fwd};
+    ev.mark(5, s);
     hipLaunchKernelGGL(dlogits_kernel<T>, dim3(tiles_v * tiles_t), dim3(kThreads), 0, s, d,
                        tiles_v, tiles_t);
+    ev.mark(6, s);
     TargetArgs fx{(const char*)a.H + c0 * D * esz, a.W, a.y + c0, cmask, nc, D, a.v_real,
                   a.ignore_index, a.inv_tau, 1, nullptr, a.lse + c0, a.coef + c0,
                   a.grad_output, dz, VK};
     hipError_t e0 = launch_target_logit(sizeof(T) == 2 ? 0 : 1, fx, s);
     if (e0 != hipSuccess) return e0;
-    ev.mark(6, s);
+    ev.mark(7, s);
 
     // dH rows of the chunk: M = d (WT rows), N = t (dz rows), K = v
     ProductArgs ph{k_panel(wt, VK * esz, D), k_panel(dz, VK * esz, nc), VK * esz,
                    a.dH + c0 * D, D, D, nc, INT64_MAX, 0, a.group_dh};
-    hipLaunchKernelGGL(product_kernel<T>, dim3(tiles_d * tiles_t), dim3(kThreads), 0, s, ph,
+    hipLaunchKernelGGL((product_kernel<T, 0>), dim3(tiles_d * tiles_t), dim3(kThreads), 0, s, ph,
                        tiles_d, tiles_t);
-    ev.mark(7, s);
+    ev.mark(8, s);
 
     // dzT: rows v, K = t;  HT: rows d, K = t
     transpose_panel<E>(dz, 0, true, VK * esz, ncp, VK, dzt, VK, ncp, s);
     transpose_panel<E>((const char*)a.H + c0 * D * esz, D, false, 0, nc, D, ht, Dp, ncp, s);
-    ev.mark(8, s);
+    ev.mark(9, s);
 
     // dW: M = d (HT rows), N = v (dzT rows), K = t
     ProductArgs pw{k_panel(ht, ncp * esz, D), k_panel(dzt, ncp * esz, VK), ncp * esz,
                    a.dW, D, D, (a.v_rows < VK ? a.v_rows : VK), a.v_real, c0 > 0 ? 1 : 0,
                    a.group_dw};
-    hipLaunchKernelGGL(product_kernel<T>, dim3(tiles_d * tiles_v), dim3(kThreads), 0, s, pw,
+    hipLaunchKernelGGL((product_kernel<T, 1>), dim3(tiles_d * tiles_v), dim3(kThreads), 0, s, pw,
                        tiles_d, tiles_v);
-    ev.mark(9, s);
+    ev.mark(10, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

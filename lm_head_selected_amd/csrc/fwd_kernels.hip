@@ -174,23 +174,26 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 }
 
 template <typename T>
-static void launch_tiles(const FwdTileArgs& a, int tiles_m, int tiles_n, hipStream_t s) {
+static void launch_tiles(const FwdTileArgs& a, int tiles_m, int tiles_n,
+                         const StageEvents& ev, hipStream_t s) {
   // every tile but the last is entirely inside the real vocabulary
   const int full = (a.v_real % kTile == 0) ? tiles_m : tiles_m - 1;
   if (full > 0)
     hipLaunchKernelGGL((fwd_tile_kernel<T, false>), dim3(full * tiles_n), dim3(kThreads), 0, s,
                        a, 0, full, tiles_n);
+  ev.mark(1, s);
   if (full < tiles_m)
     hipLaunchKernelGGL((fwd_tile_kernel<T, true>), dim3(tiles_n), dim3(kThreads), 0, s, a, full,
                        1, tiles_n);
 }
 
-hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt, hipStream_t s) {
+hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt,
+                            const StageEvents& ev, hipStream_t s) {
   const int tiles_m = (int)n_vt;
   const int tiles_n = (int)ceil_div(a.n_tokens, kTokenTile);
   if (tiles_m * tiles_n == 0) return hipSuccess;
-  if (dtype == 0) launch_tiles<__bf16>(a, tiles_m, tiles_n, s);
-  else launch_tiles<float>(a, tiles_m, tiles_n, s);
+  if (dtype == 0) launch_tiles<__bf16>(a, tiles_m, tiles_n, ev, s);
+  else launch_tiles<float>(a, tiles_m, tiles_n, ev, s);
   return hipGetLastError();
 }
 

@@ -230,9 +230,8 @@ int grpo_head_fwd(const grpo_head_params* p, const void* H, const void* W, const
     g_marks.mark(0, s);
     gh::FwdTileArgs fa{W, H, p->n_tokens, p->d_model, p->v_real, p->inv_tau,
                        (float2*)(w + L.partials), kGroupFwd};
-    e = gh::launch_fwd_tiles(p->dtype, fa, L.n_vt, s);
+    e = gh::launch_fwd_tiles(p->dtype, fa, L.n_vt, g_marks, s);
     if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
-    g_marks.mark(1, s);
     gh::TargetArgs ta{H, W, y, mask, p->n_tokens, p->d_model, p->v_real, p->ignore_index,
                       p->inv_tau, 0, (float*)(w + L.zy), nullptr, nullptr, nullptr, nullptr, 0};
     e = gh::launch_target_logit(p->dtype, ta, s);

@@ -89,7 +89,9 @@ struct BwdArgs {
   const StageEvents* marks;
 };
 
-hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt, hipStream_t s);
+// records stage event 1 between the full-tile launch and the ragged-tile launch
+hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt,
+                            const StageEvents& ev, hipStream_t s);
 hipError_t launch_target_logit(int dtype, const TargetArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_loss(const LossArgs& a, hipStream_t s);
