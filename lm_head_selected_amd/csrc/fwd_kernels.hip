@@ -29,8 +29,12 @@ __device__ __forceinline__ bool token_active(const uint8_t* mask, const int64_t*
 template <typename T, bool kPartial>
 __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int tm_first,
                                                             int tiles_m, int tiles_n) {
+  // One LDS object only: with a second __shared__ array the compiler can no longer
+  // tell the direct-to-LDS loads from the fragment reads and waits for every load
+  // right after issuing it.  The per-half row statistics reuse the pipeline's
+  // buffers once the K loop has drained.
   __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
-  __shared__ float2 half_stats[2][kTile];
+  static_assert(sizeof(float2) * 2 * kTile <= kGemmLds, "row statistics fit in LDS");
 
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, a.group_m, tm, tn);
@@ -48,6 +52,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int t
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWN, wn = wave % kWN;
   const float c2 = a.inv_tau * kLog2e;
+  float2(*half_stats)[kTile] = (float2(*)[kTile])lds;   // [2][kTile]
   if (kPartial) {
     const int64_t left = a.v_real - (v0 + wm * 128);
     mask_rows(acc, (int)(left < 0 ? 0 : (left > 128 ? 128 : left)));
