@@ -30,16 +30,19 @@ __device__ __forceinline__ bool token_is_active(const uint8_t* mask, const int64
   return mask ? (mask[t] != 0) : (y[t] != ignore_index);
 }
 
+// Output tiles are written with non-temporal stores: a round of tiles writes about
+// as many bytes as an XCD's L2 holds, and ordinary stores would evict the operand
+// panels that the resident tiles are sharing.
 template <typename T> struct Store4;
 template <> struct Store4<__bf16> {
   static __device__ __forceinline__ void run(void* p, float a, float b, float c, float d) {
     bf16x4 v = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
-    *(bf16x4*)p = v;
+    __builtin_nontemporal_store(__builtin_bit_cast(i32x2, v), (i32x2*)p);
   }
 };
 template <> struct Store4<float> {
   static __device__ __forceinline__ void run(void* p, float a, float b, float c, float d) {
-    *(f32x4*)p = f32x4{a, b, c, d};
+    __builtin_nontemporal_store(f32x4{a, b, c, d}, (f32x4*)p);
   }
 };
 
@@ -81,22 +84,21 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
   const int64_t esz = Elem<T>::size;
   const Operand A = row_major(a.W, a.d_model * esz, a.v_real);
   const Operand B = row_major(a.H, a.d_model * esz, a.chunk_tokens);
-  f32x16 acc[kBI][kBJ];
+  f32x4 acc[kBI][kBJ];
   zero_acc(acc);
   gemm_tile<T>(A, B, v0, t0, a.d_model * esz, (lds_t*)lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWN, wn = wave % kWN;
-  const int64_t vbase = v0 + wm * (kTile / kWM);
+  const int64_t vbase = v0 + wm * (kTile / kWM) + (lane >> 4) * 4;
   const float c2 = a.inv_tau * kLog2e;
-  const int hi = lane >> 5;
   const int64_t kb = a.v_k * esz;   // bytes of one dz row along K (vocabulary)
   // (g, lse2) of the lane's token columns; tokens past the chunk read zeros
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gl, (uint32_t)(a.chunk_tokens * 8));
 
 #pragma unroll
   for (int j = 0; j < kBJ; ++j) {
-    const int64_t t = t0 + wn * (kTile / kWN) + j * 32 + (lane & 31);
+    const int64_t t = t0 + wn * (kTile / kWN) + j * 16 + (lane & 15);
     // (cast the whole vector: clang miscompiles bit_cast of a single vector element)
     const f32x2 glv = __builtin_bit_cast(
         f32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, (uint32_t)(t * 8), 0, 0));
@@ -104,16 +106,14 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
     const float lse2 = glv[1];
     char* rowp = (char*)a.dz + (t >> 8) * 256 * kb + (t & 255) * 128;
 #pragma unroll
-    for (int i = 0; i < kBI; ++i)
+    for (int i = 0; i < kBI; ++i) {
+      const int64_t v = vbase + i * 16;   // 4 consecutive vocabulary rows
+      float d[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t v = vbase + i * 32 + q * 8 + hi * 4;   // 4 consecutive vocabulary rows
-        float d[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[e] = -g * fast_exp2(acc[i][j][q * 4 + e] * c2 - lse2);
-        const int64_t vb = v * esz;
-        Store4<T>::run(rowp + (vb >> 7) * (256 * 128) + (vb & 127), d[0], d[1], d[2], d[3]);
-      }
+      for (int e = 0; e < 4; ++e) d[e] = -g * fast_exp2(acc[i][j][e] * c2 - lse2);
+      const int64_t vb = v * esz;
+      Store4<T>::run(rowp + (vb >> 7) * (256 * 128) + (vb & 127), d[0], d[1], d[2], d[3]);
+    }
   }
 }
 
@@ -138,31 +138,28 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, a.group_m, tm, tn);
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
-  f32x16 acc[kBI][kBJ];
+  f32x4 acc[kBI][kBJ];
   zero_acc(acc);
   gemm_tile<T>(a.A, a.B, m0, n0, a.k_bytes, (lds_t*)lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWN, wn = wave % kWN;
-  const int hi = lane >> 5;
+  const int64_t mbase = m0 + wm * (kTile / kWM) + (lane >> 4) * 4;
 #pragma unroll
   for (int j = 0; j < kBJ; ++j) {
-    const int64_t n = n0 + wn * (kTile / kWN) + j * 32 + (lane & 31);
+    const int64_t n = n0 + wn * (kTile / kWN) + j * 16 + (lane & 15);
     if (n >= a.n_limit) continue;
     const bool zero = n >= a.n_zero_from;
     float* rowp = a.out + n * a.ld_out;
 #pragma unroll
-    for (int i = 0; i < kBI; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t m = m0 + wm * (kTile / kWM) + i * 32 + q * 8 + hi * 4;
-        if (m >= a.m_limit) continue;
-        f32x4 v = {acc[i][j][q * 4], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2],
-                   acc[i][j][q * 4 + 3]};
-        if (zero) v = f32x4{0.f, 0.f, 0.f, 0.f};
-        else if (a.accumulate) v += *(const f32x4*)(rowp + m);
-        *(f32x4*)(rowp + m) = v;
-      }
+    for (int i = 0; i < kBI; ++i) {
+      const int64_t m = mbase + i * 16;   // 4 consecutive M
+      if (m >= a.m_limit) continue;
+      f32x4 v = acc[i][j];
+      if (zero) v = f32x4{0.f, 0.f, 0.f, 0.f};
+      else if (a.accumulate) v += *(const f32x4*)(rowp + m);
+      __builtin_nontemporal_store(v, (f32x4*)(rowp + m));
+    }
   }
 }
 

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int t
 
   const Operand A = row_major(a.W, a.d_model * esz, a.v_real);
   const Operand B = row_major(a.H, a.d_model * esz, a.n_tokens);
-  f32x16 acc[kBI][kBJ];
+  f32x4 acc[kBI][kBJ];
   zero_acc(acc);
   gemm_tile<T>(A, B, v0, t0, a.d_model * esz, (lds_t*)lds, acc);
 
@@ -58,27 +58,30 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int t
     mask_rows(acc, (int)(left < 0 ? 0 : (left > 128 ? 128 : left)));
   }
 
+  // column block j: token tl; the four 16-lane groups hold different rows of it
 #pragma unroll
   for (int j = 0; j < kBJ; ++j) {
-    const int tl = wn * (kTile / kWN) + j * 32 + (lane & 31);
+    const int tl = wn * (kTile / kWN) + j * 16 + (lane & 15);
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kBI; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < 4; ++e) {
         acc[i][j][e] *= c2;          // padded rows stay -inf (c2 > 0)
         m = fmaxf(m, acc[i][j][e]);
       }
+    m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
     float s = 0.0f;
     if (!kPartial || m != -INFINITY) {
 #pragma unroll
       for (int i = 0; i < kBI; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s += fast_exp2(acc[i][j][e] - m);
+        for (int e = 0; e < 4; ++e) s += fast_exp2(acc[i][j][e] - m);
     }
+    s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
-    // both lane halves hold the same (m, s); both write it
+    // all four lane groups hold the same (m, s); all write it
     half_stats[wm][tl] = make_float2(m, s);
   }
   __syncthreads();

@@ -6,7 +6,7 @@
 // are written in.  Accumulation is fp32.
 //
 //  * 512 threads = 8 waves in a 2 (M) x 4 (N) grid; each wave owns a 128x64
-//    sub-tile as 4x2 blocks of 32x32 MFMA accumulators (128 fp32 per lane), so
+//    sub-tile as 8x4 blocks of 16x16 MFMA accumulators (128 fp32 per lane), so
 //    two waves share each SIMD and the hardware issues one wave's MFMAs while the
 //    other waits on memory or a barrier.
 //  * K advances 128 bytes per stage (64 bf16 or 32 fp32); one stage of A and B is
@@ -22,17 +22,21 @@
 //    being read.
 //  * LDS rows are 128 B (8 chunks of 16 B); chunk c of row r is stored at chunk
 //    c ^ ((r >> 1) & 7).  gfx950's LDS has 64 banks (256 B) and serves a 16-byte
-//    read for 16 lanes per pass; a fragment read has 16 lanes on 16 consecutive
-//    rows at one logical chunk, i.e. physical (r & 1, c ^ ((r >> 1) & 7)), all
-//    distinct, so every pass touches each bank once.
-//  * bf16: v_mfma_f32_32x32x16_bf16, one per 16-B fragment pair.  fp32:
-//    v_mfma_f32_32x32x2_f32, four per fragment pair (exact fp32 products).
+//    read for 16 lanes per pass; a fragment read has each group of 16 lanes on 16
+//    consecutive rows at one logical chunk, i.e. physical (r & 1, c ^ ((r >> 1) & 7)),
+//    all distinct, so every pass touches each bank once.
+//  * bf16: v_mfma_f32_16x16x32_bf16, one per 16-B fragment pair.  fp32:
+//    v_mfma_f32_16x16x4_f32, four per fragment pair (exact fp32 products).  Under
+//    the chip's power limit the 16x16x32 form sustains a markedly higher clock
+//    than 32x32x16 on random operands at the same MFMA occupancy.
+//  * A fragment (16 B per lane) is row (16-row block origin + lane % 16), K bytes
+//    16 * (4 ks + lane / 16) of the stage: the 16x16x32 operand layout.
 //
-// Accumulator layout (per wave, block (i, j), element e of the 16), relative to
+// Accumulator layout (per wave, block (i, j), element e of the 4), relative to
 // the wave's sub-tile at (wm * 128, wn * 64):
-//   row (M) = i*32 + (e >> 2)*8 + (lane >> 5)*4 + (e & 3)
-//   col (N) = j*32 + (lane & 31)
-// so each lane holds 4 consecutive M indices for one N index per (i, j, e>>2).
+//   row (M) = i*16 + (lane >> 4)*4 + e
+//   col (N) = j*16 + (lane & 15)
+// so each lane holds 4 consecutive M indices for one N index per (i, j).
 #pragma once
 
 #include "device_common.hpp"
@@ -43,8 +47,8 @@ constexpr int kTile = 256;
 constexpr int kWM = 2, kWN = 4;                 // wave grid
 constexpr int kWaves = kWM * kWN;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBI = kTile / kWM / 32;           // 32-row accumulator blocks per wave (M)
-constexpr int kBJ = kTile / kWN / 32;           // 32-col accumulator blocks per wave (N)
+constexpr int kBI = kTile / kWM / 16;           // 16-row accumulator blocks per wave (M)
+constexpr int kBJ = kTile / kWN / 16;           // 16-col accumulator blocks per wave (N)
 // K pipeline: 128-byte K stages, 2 LDS buffers (128 KB)
 constexpr int kRowB = 128;
 constexpr int kNst = 2;
@@ -75,18 +79,18 @@ __host__ __device__ inline int64_t k_panel_offset(int64_t row, int64_t kb, int64
 
 template <typename T> struct Mma;
 template <> struct Mma<__bf16> {
-  static __device__ __forceinline__ void run(f32x16& c, i32x4 a, i32x4 b) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+  static __device__ __forceinline__ void run(f32x4& c, i32x4 a, i32x4 b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
 };
 template <> struct Mma<float> {
-  static __device__ __forceinline__ void run(f32x16& c, i32x4 a, i32x4 b) {
+  static __device__ __forceinline__ void run(f32x4& c, i32x4 a, i32x4 b) {
     const f32x4 af = __builtin_bit_cast(f32x4, a), bf = __builtin_bit_cast(f32x4, b);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[0], bf[0], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[1], bf[1], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[2], bf[2], c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[3], bf[3], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[0], bf[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[1], bf[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[2], bf[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(af[3], bf[3], c, 0, 0, 0);
   }
 };
 
@@ -125,7 +129,7 @@ template <int ROWB, int NST> struct Pipe {
   static constexpr int kStage = 2 * kTile * ROWB;       // A + B bytes per stage
   static constexpr int kLds = NST * kStage;
   static constexpr int kRowsPerLoad = 1024 / ROWB;      // rows one wave-wide load covers
-  static constexpr int kKs = ROWB / 32;                 // 16-element bf16 K sub-steps
+  static constexpr int kKs = ROWB / 64;                 // 32-element bf16 K sub-steps
   // physical chunk of logical chunk c in row r; 16 consecutive rows read at one
   // logical chunk land on 16 distinct 16-byte bank groups of the 64-bank LDS
   static __device__ __forceinline__ int swz(int r) {
@@ -143,7 +147,7 @@ constexpr int kGemmLds = Pipe<kRowB, kNst>::kLds;
 // bytes land at the block base + 16 l, so the lane fetches the logical chunk
 // that belongs at that physical position of the swizzled row).  Iteration s:
 //   issue the loads of stage s + NST - 1 (into the buffer stage s - 1 used);
-//   for each 16-element sub-step: read the next fragments, run 16 MFMAs on the
+//   for each 32-element sub-step: read the next fragments, run 32 MFMAs on the
 //   current ones; before the last sub-step's MFMAs, wait for stage s + 1's loads,
 //   barrier, and read stage s + 1's first fragments, so that LDS latency hides
 //   under those MFMAs.
@@ -155,7 +159,7 @@ constexpr int kGemmLds = Pipe<kRowB, kNst>::kLds;
 template <typename T, int ROWB = kRowB, int NST = kNst>
 __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, int64_t m0,
                                           int64_t n0, int64_t k_bytes, lds_t* lds,
-                                          f32x16 (&acc)[kBI][kBJ]) {
+                                          f32x4 (&acc)[kBI][kBJ]) {
   typedef Pipe<ROWB, NST> P;
   static_assert(ROWB == 128, "operand stage strides assume 128-byte stages");
   constexpr int kLoads = kTile / P::kRowsPerLoad / kWaves;   // per wave per operand
@@ -178,13 +182,13 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   const uint32_t stepB = (uint32_t)(kWaves * P::kRowsPerLoad * B.ld_bytes);
   const uint32_t kstA = (uint32_t)A.stage_bytes, kstB = (uint32_t)B.stage_bytes;
 
-  // fragment reads: row (wave origin + 32 i + (lane & 31)), logical chunk 2 ks + (lane >> 5)
-  const int frow = lane & 31, fhalf = lane >> 5;
+  // fragment reads: row (wave origin + 16 i + (lane & 15)), logical chunk 4 ks + (lane >> 4)
+  const int frow = lane & 15, fquad = lane >> 4;
   const int fA = (wm * (kTile / kWM) + frow) * ROWB;
   const int fB = kTile * ROWB + (wn * (kTile / kWN) + frow) * ROWB;
   int fswz[P::kKs];
 #pragma unroll
-  for (int ks = 0; ks < P::kKs; ++ks) fswz[ks] = (((2 * ks + fhalf) ^ P::swz(frow)) << 4);
+  for (int ks = 0; ks < P::kKs; ++ks) fswz[ks] = (((4 * ks + fquad) ^ P::swz(frow)) << 4);
 
   const int nk = (int)(k_bytes / ROWB);
 
@@ -203,9 +207,9 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   auto read_frags = [&](i32x4 (&fa)[kBI], i32x4 (&fb)[kBJ], int stage, int ks) {
     const lds_t* s = lds + (stage % NST) * P::kStage;
 #pragma unroll
-    for (int i = 0; i < kBI; ++i) fa[i] = lds_read16(s + fA + i * 32 * ROWB + fswz[ks]);
+    for (int i = 0; i < kBI; ++i) fa[i] = lds_read16(s + fA + i * 16 * ROWB + fswz[ks]);
 #pragma unroll
-    for (int j = 0; j < kBJ; ++j) fb[j] = lds_read16(s + fB + j * 32 * ROWB + fswz[ks]);
+    for (int j = 0; j < kBJ; ++j) fb[j] = lds_read16(s + fB + j * 16 * ROWB + fswz[ks]);
   };
   auto mma = [&](const i32x4 (&fa)[kBI], const i32x4 (&fb)[kBJ]) {
 #pragma unroll
@@ -252,25 +256,23 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
 // Set every accumulator whose wave-local M row (0..127) is >= vlim to -inf.
 // Used once per tile, only on the tile holding the vocabulary's ragged end;
 // each row mask serves the four column blocks and dies.
-__device__ __forceinline__ void mask_rows(f32x16 (&acc)[kBI][kBJ], int vlim) {
-  const int hi = (threadIdx.x & 63) >> 5;
+__device__ __forceinline__ void mask_rows(f32x4 (&acc)[kBI][kBJ], int vlim) {
+  const int q = (threadIdx.x & 63) >> 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kBI; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const bool pad = i * 32 + (e >> 2) * 8 + hi * 4 + (e & 3) >= vlim;
+    for (int e = 0; e < 4; ++e) {
+      const bool pad = i * 16 + q * 4 + e >= vlim;
 #pragma unroll
       for (int j = 0; j < kBJ; ++j) acc[i][j][e] = pad ? -INFINITY : acc[i][j][e];
     }
 }
 
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[kBI][kBJ]) {
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[kBI][kBJ]) {
 #pragma unroll
   for (int i = 0; i < kBI; ++i)
 #pragma unroll
-    for (int j = 0; j < kBJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    for (int j = 0; j < kBJ; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
 }  // namespace gh

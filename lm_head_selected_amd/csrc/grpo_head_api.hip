@@ -122,7 +122,7 @@ gh::WsLayout layout(const grpo_head_params* p, bool with_gemm = true) {
 }
 
 // Tile-order group sizes (M-tiles walked per N-tile), chosen by measurement.
-constexpr int kGroupFwd = 8, kGroupDh = 16, kGroupDw = 16;
+constexpr int kGroupFwd = 8, kGroupDh = 4, kGroupDw = 4;
 
 int finish_validation(uint32_t* dflags, hipStream_t s, bool check_active) {
   uint32_t h[2] = {0, 0};
