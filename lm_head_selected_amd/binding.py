@@ -30,7 +30,7 @@ EXPORTS = ("grpo_head_fwd_workspace_size", "grpo_head_workspace_size",
 N_STAGE_EVENTS = 11
 STAGES = {"fwd_tiles": (0, 1), "fwd_tail": (1, 2), "fwd_objective": (2, 3),
           "bwd_prep": (4, 5), "bwd_dlogits": (5, 6), "bwd_target": (6, 7),
-          "bwd_dh": (7, 8), "bwd_transposes": (8, 9), "bwd_dw": (9, 10)}
+          "bwd_dh": (7, 8), "bwd_dw": (9, 10)}
 # stages that are exactly one matrix-core launch, with that launch's kernel symbol stem
 GEMM_STAGES = {"fwd_tiles": "fwd_tile_kernel", "bwd_dlogits": "dlogits_kernel",
                "bwd_dh": "product_kernel<__bf16, 0>", "bwd_dw": "product_kernel<__bf16, 1>"}

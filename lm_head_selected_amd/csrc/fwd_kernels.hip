@@ -43,11 +43,12 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int t
   const int64_t t0 = (int64_t)tn * kTile;   // tokens of this tile
   const int64_t esz = Elem<T>::size;
 
-  const Operand A = row_major(a.W, a.d_model * esz, a.v_real);
-  const Operand B = row_major(a.H, a.d_model * esz, a.n_tokens);
+  const Operand A = nt_row_major(a.W, a.d_model * esz, a.v_real);
+  const Operand B = nt_row_major(a.H, a.d_model * esz, a.n_tokens);
   f32x4 acc[kBI][kBJ];
   zero_acc(acc);
-  gemm_tile<T>(A, B, v0, t0, a.d_model * esz, (lds_t*)lds, acc);
+  gemm_tile<T, false, false>(A, B, v0, t0, (int)(a.d_model * esz / kStageBytes), (lds_t*)lds,
+                             acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWN, wn = wave % kWN;
@@ -148,8 +149,8 @@ __global__ __launch_bounds__(256) void target_logit_kernel(TargetArgs a) {
     const float g = a.grad_output ? *a.grad_output * a.coef[t] * a.inv_tau
                                   : a.coef[t] * a.inv_tau;
     const float v = g * (1.0f - fast_exp2((z - a.lse[t]) * kLog2e));
-    // dz is in K-panel layout: rows = tokens, K = vocabulary
-    char* p = (char*)a.dz + k_panel_offset(t, yy * (int64_t)sizeof(T), a.v_k * (int64_t)sizeof(T));
+    // dz is v-tiled: [vocabulary / 256][dz_rows][256]
+    char* p = (char*)a.dz + vtiled_offset(t, yy, a.dz_rows, (int64_t)sizeof(T));
     if (sizeof(T) == 2) *(__bf16*)p = (__bf16)v;
     else *(float*)p = v;
   }

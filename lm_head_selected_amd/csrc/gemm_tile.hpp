@@ -1,36 +1,39 @@
-// One 256x256 output tile of C = A . B^T on gfx950 matrix cores.
+// One 256x256 output tile of C[m][n] = sum_k A(m, k) B(n, k) on gfx950 matrix
+// cores, fp32 accumulation.
 //
-// A [M][K] and B [N][K] are row-major with K contiguous ("NT"): the layout of
-// the LM-head weight (vocab rows, hidden contiguous) and of the hidden states
-// (token rows, hidden contiguous), and the layout the backward's staging buffers
-// are written in.  Accumulation is fp32.
+// Operands come in two orientations:
+//  * NT ("K-contiguous"): the operand is stored with rows = M (or N) indices and K
+//    contiguous in a row: the LM-head weight W [v][d] and the hidden states H [t][d]
+//    in the logit product, and dz [t][v] in the dH product.
+//  * MN ("MN-contiguous"): rows = K indices, M (or N) contiguous: W [v][d] and
+//    H [t][d] as the d-side of the dH / dW products, and dz [t][v] as the v-side of
+//    the dW product.  Fragments are read from LDS with the transposing
+//    ds_read_b64_tr_b16 (bf16), so no operand is ever transposed in memory.
 //
+// Geometry and pipeline:
 //  * 512 threads = 8 waves in a 2 (M) x 4 (N) grid; each wave owns a 128x64
 //    sub-tile as 8x4 blocks of 16x16 MFMA accumulators (128 fp32 per lane), so
 //    two waves share each SIMD and the hardware issues one wave's MFMAs while the
 //    other waits on memory or a barrier.
-//  * K advances 128 bytes per stage (64 bf16 or 32 fp32); one stage of A and B is
-//    2 x 32 KB of LDS, double buffered (128 KB of the CU's 160 KB).
-//  * Operands are either row-major (the caller's W and H: rows ld_bytes apart,
-//    a stage 128 bytes further along the row) or K-panel (the backward's own
-//    staging buffers: each 256-row tile stores its K stages one after another,
-//    256 x 128 contiguous bytes per stage), which keeps every stage of a tile in
-//    one small address range.
-//  * Global -> LDS through direct-to-LDS raw buffer loads (no register staging).
-//    Rows at or beyond the operand's valid row count fall outside the buffer
-//    resource and load as zeros, which also keeps padded vocabulary rows from ever
-//    being read.
-//  * LDS rows are 128 B (8 chunks of 16 B); chunk c of row r is stored at chunk
-//    c ^ ((r >> 1) & 7).  gfx950's LDS has 64 banks (256 B) and serves a 16-byte
-//    read for 16 lanes per pass; a fragment read has each group of 16 lanes on 16
-//    consecutive rows at one logical chunk, i.e. physical (r & 1, c ^ ((r >> 1) & 7)),
-//    all distinct, so every pass touches each bank once.
-//  * bf16: v_mfma_f32_16x16x32_bf16, one per 16-B fragment pair.  fp32:
-//    v_mfma_f32_16x16x4_f32, four per fragment pair (exact fp32 products).  Under
-//    the chip's power limit the 16x16x32 form sustains a markedly higher clock
-//    than 32x32x16 on random operands at the same MFMA occupancy.
-//  * A fragment (16 B per lane) is row (16-row block origin + lane % 16), K bytes
-//    16 * (4 ks + lane / 16) of the stage: the 16x16x32 operand layout.
+//  * bf16: v_mfma_f32_16x16x32_bf16, one per fragment pair.  Under the chip's power
+//    limit this form sustains a markedly higher clock than 32x32x16 on random
+//    operands at the same MFMA occupancy.  fp32: v_mfma_f32_16x16x4_f32, four per
+//    fragment pair (exact fp32 products).
+//  * K advances 128 bytes per stage (64 bf16 or 32 fp32); a stage is 32 KB of A and
+//    32 KB of B in LDS, double buffered (128 KB of the CU's 160 KB).
+//  * Global -> LDS through direct-to-LDS raw buffer loads, 16 B per lane, every
+//    wave-wide load filling 1 KB of LDS.  Bytes outside an operand's buffer range
+//    load as zeros; the ranges are set so that no invalid row (padded vocabulary,
+//    tokens past the batch) is ever read.
+//  * NT stage layout: 256 rows x 128 B; chunk c of row r sits at chunk
+//    c ^ ((r >> 1) & 7).  A fragment read (ds_read_b128) has each group of 16 lanes
+//    on 16 consecutive rows at one logical chunk: 16 distinct bank groups of the
+//    64-bank LDS.
+//  * MN stage layout (bf16): 64 K-rows x 512 B; 32-byte segment s of K-row k sits
+//    at segment s ^ sw(k), sw(k) = (k & 3) | ((k >> 1) & 4).  One pass of a
+//    transposing read serves 32 lanes on 8 K-rows at one logical segment: 8
+//    distinct bank groups.  (fp32 MN: 32 K-rows x 1 KB, unswizzled, read with
+//    ds_read_b32; the fp32 path exists for exactness, not speed.)
 //
 // Accumulator layout (per wave, block (i, j), element e of the 4), relative to
 // the wave's sub-tile at (wm * 128, wn * 64):
@@ -49,33 +52,116 @@ constexpr int kWaves = kWM * kWN;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBI = kTile / kWM / 16;           // 16-row accumulator blocks per wave (M)
 constexpr int kBJ = kTile / kWN / 16;           // 16-col accumulator blocks per wave (N)
-// K pipeline: 128-byte K stages, 2 LDS buffers (128 KB)
-constexpr int kRowB = 128;
-constexpr int kNst = 2;
+constexpr int kStageBytes = 128;                // K bytes per stage
+constexpr int kOpLds = kTile * kStageBytes;     // one operand's stage: 32 KB
+constexpr int kStageLds = 2 * kOpLds;           // A + B
+constexpr int kGemmLds = 2 * kStageLds;         // two stage buffers: 128 KB
+constexpr int kLoads = kOpLds / 1024 / kWaves;  // wave-wide 1 KB loads per operand and stage
 
-// Addressing of an operand: byte (row r of tile t, stage s, chunk c) lives at
-//   base + t * tile_bytes + (r % 256) * ld_bytes + s * stage_bytes + 16 c.
+// Addressing of an operand.  For the tile holding M/N indices [256 t, 256 t + 256):
+//   base_t = base + t * tile_bytes, valid for clamp(span - t * tile_bytes, 0, cap)
+//   bytes from base_t; bytes beyond load as zeros.
+// NT: byte (row r of the tile, K byte kb) = r * ld + stage_off(kb / 128) + kb % 128,
+//     stage_off(s) = (s >> group_shift) * group_bytes + (s & (2^group_shift - 1)) * 128.
+// MN: byte (K row k, element r of the tile) = k * ld + r * element size.
 struct Operand {
-  const char* base;     // element (0, 0)
-  int64_t ld_bytes;     // bytes between rows of a tile (row-major: the row pitch)
-  int64_t stage_bytes;  // bytes between K stages (row-major: 128)
-  int64_t tile_bytes;   // bytes between 256-row tiles (row-major: 256 * pitch)
-  int64_t rows;         // valid rows; row-major rows beyond load as zero
-  bool panel;           // K-panel layout: every row of every tile is initialised
+  const char* base;
+  int64_t ld;           // bytes between rows (NT: M/N rows; MN: K rows)
+  int64_t tile_bytes;   // bytes between 256-wide M/N tiles
+  int64_t span;         // valid bytes from base (see above)
+  int64_t cap;          // most bytes one tile's resource may cover
+  int64_t group_bytes;  // NT: bytes between K-stage groups
+  int32_t group_shift;  // NT: log2(stages per group)
+  int32_t mn;           // 1: MN-contiguous
 };
 
-__host__ __device__ inline Operand row_major(const void* base, int64_t pitch, int64_t rows) {
-  return Operand{(const char*)base, pitch, 128, 256 * pitch, rows, false};
+// Row-major [rows][K] with K contiguous (pitch bytes per row); rows >= `rows` load
+// as zeros.
+__host__ __device__ inline Operand nt_row_major(const void* base, int64_t pitch, int64_t rows) {
+  return Operand{(const char*)base, pitch, 256 * pitch, rows * pitch, 256 * pitch, 0, 30, 0};
 }
-// K-panel layout of a [rows_pad][k_bytes] matrix (rows_pad a multiple of 256)
-__host__ __device__ inline Operand k_panel(const void* base, int64_t k_bytes, int64_t rows) {
-  return Operand{(const char*)base, 128, 256 * 128, 256 * k_bytes, rows, true};
+// The v-tiled layout [groups][rows_pad][256 elements] (dz) read K-contiguous with
+// rows = its rows and K = the 256-element groups in order.
+__host__ __device__ inline Operand nt_vtiled(const void* base, int64_t rows_pad, int64_t esz,
+                                            int64_t total_bytes) {
+  const int32_t shift = esz == 2 ? 2 : 3;   // 128-byte stages per 256-element group
+  return Operand{(const char*)base, 256 * esz, 256 * 256 * esz, total_bytes, total_bytes,
+                 rows_pad * 256 * esz, shift, 0};
 }
-// Byte offset of (row, byte kb along K) in the K-panel layout of a matrix whose
-// rows hold k_bytes.
-__host__ __device__ inline int64_t k_panel_offset(int64_t row, int64_t kb, int64_t k_bytes) {
-  return (row >> 8) * 256 * k_bytes + (kb >> 7) * (256 * 128) + (row & 255) * 128 + (kb & 127);
+// Row-major [k_rows][cols] (pitch bytes per row) read MN-contiguous, K = its rows:
+// K rows >= k_rows and columns >= cols of the last valid row load as zeros.
+__host__ __device__ inline Operand mn_row_major(const void* base, int64_t pitch, int64_t k_rows,
+                                               int64_t cols, int64_t esz) {
+  return Operand{(const char*)base, pitch, 256 * esz,
+                 k_rows > 0 ? (k_rows - 1) * pitch + cols * esz : 0, (int64_t)1 << 62, 0, 30, 1};
 }
+// The v-tiled layout read MN-contiguous: K = its rows, M/N = the elements.
+__host__ __device__ inline Operand mn_vtiled(const void* base, int64_t rows_pad, int64_t esz,
+                                            int64_t groups) {
+  const int64_t tb = rows_pad * 256 * esz;
+  return Operand{(const char*)base, 256 * esz, tb, groups * tb, tb, 0, 30, 1};
+}
+// Byte offset of (row, element v) in the v-tiled layout.
+__host__ __device__ inline int64_t vtiled_offset(int64_t row, int64_t v, int64_t rows_pad,
+                                                 int64_t esz) {
+  return (v >> 8) * rows_pad * 256 * esz + row * 256 * esz + (v & 255) * esz;
+}
+
+// Base and valid byte count of one M/N tile of an operand.
+struct TileRange {
+  const char* base;
+  int64_t limit;
+};
+__device__ __forceinline__ TileRange tile_range(const Operand& op, int64_t r0) {
+  const int64_t t = r0 >> 8;
+  int64_t n = op.span - t * op.tile_bytes;
+  n = n < 0 ? 0 : (n > op.cap ? op.cap : n);
+  return TileRange{op.base + t * op.tile_bytes, n};
+}
+
+// Byte offset of K stage s from the tile base (64-bit: operands may exceed 4 GB).
+template <typename T>
+__device__ __forceinline__ int64_t stage_off(const Operand& op, int s) {
+  if (op.mn) return (int64_t)s * (kStageBytes / (int)sizeof(T)) * op.ld;
+  return (int64_t)(s >> op.group_shift) * op.group_bytes +
+         (int64_t)(s & ((1 << op.group_shift) - 1)) * kStageBytes;
+}
+
+// Buffer resource of one K stage of a tile: based at the stage, so per-lane
+// offsets stay small; bytes past the tile's valid range load as zeros.  (The
+// clamp is written on 32-bit halves so it stays in scalar registers.)
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(const Operand& op,
+                                                             const TileRange& tr, int s) {
+  const int64_t o = stage_off<T>(op, s);
+  const int64_t n = tr.limit - o;
+  const int32_t hi = (int32_t)(n >> 32);
+  const uint32_t lo = (uint32_t)n;
+  const uint32_t rec = hi < 0 ? 0u : (hi > 0 ? 0xffffffffu : lo);
+  // every field is wave-uniform; say so, so the resource lives in scalar registers
+  const uint64_t b = (uint64_t)(uintptr_t)(tr.base + o);
+  const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return make_rsrc((const void*)(uintptr_t)(((uint64_t)bhi << 32) | blo),
+                   __builtin_amdgcn_readfirstlane(rec));
+}
+
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes at voffset + soffset of
+// the resource land at LDS byte lds_addr + 16 l.  Issued as inline assembly so
+// that the compiler does not treat the in-flight LDS writes as aliasing every
+// later LDS read (it would wait for all loads before each read); the pipeline
+// waits for these loads explicitly.  M0 holds the LDS address; nothing else in
+// these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                      uint32_t soffset, uint32_t lds_addr) {
+  __asm__ volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                   :
+                   : "v"(voffset), "s"(r), "s"(soffset), "s"(lds_addr)
+                   : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 template <typename T> struct Mma;
 template <> struct Mma<__bf16> {
@@ -94,18 +180,20 @@ template <> struct Mma<float> {
   }
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const Operand& op, int64_t r0) {
-  const char* base = op.base + (r0 >> 8) * op.tile_bytes;
-  if (op.panel) return make_rsrc(base, (uint32_t)op.tile_bytes);
-  int64_t valid = op.rows - r0;
-  valid = valid < 0 ? 0 : (valid > kTile ? kTile : valid);
-  return make_rsrc(base, (uint32_t)(valid * op.ld_bytes));
-}
-
 typedef __attribute__((address_space(3))) char lds_t;
 
 __device__ __forceinline__ i32x4 lds_read16(const lds_t* p) {
   return *(const __attribute__((address_space(3))) i32x4*)p;
+}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+// Transposing LDS read (ds_read_b64_tr_b16): 8 bytes per lane, redistributed within
+// each group of 16 lanes.
+__device__ __forceinline__ i32x2 lds_read_tr16(const lds_t* p) {
+  return __builtin_bit_cast(
+      i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p));
+}
+__device__ __forceinline__ int lds_read4(const lds_t* p) {
+  return *(const __attribute__((address_space(3))) int*)p;
 }
 
 template <int N> __device__ __forceinline__ void wait_vm() {
@@ -120,96 +208,116 @@ __device__ __forceinline__ void pipe_barrier() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Shape of the K pipeline: ROWB bytes of K per stage and row (64 or 128) and
-// NST stage buffers in LDS (loads run NST - 1 stages ahead of the MFMAs).
-template <int ROWB, int NST> struct Pipe {
-  static_assert(ROWB == 64 || ROWB == 128, "stage row bytes");
-  static_assert(NST >= 2 && NST <= 5, "stages");
-  static constexpr int kChunks = ROWB / 16;             // 16-byte chunks per row
-  static constexpr int kStage = 2 * kTile * ROWB;       // A + B bytes per stage
-  static constexpr int kLds = NST * kStage;
-  static constexpr int kRowsPerLoad = 1024 / ROWB;      // rows one wave-wide load covers
-  static constexpr int kKs = ROWB / 64;                 // 32-element bf16 K sub-steps
-  // physical chunk of logical chunk c in row r; 16 consecutive rows read at one
-  // logical chunk land on 16 distinct 16-byte bank groups of the 64-bank LDS
-  static __device__ __forceinline__ int swz(int r) {
-    return ROWB == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+// NT stage swizzle: physical 16-B chunk of logical chunk c in row r is c ^ swz_nt(r)
+__device__ __forceinline__ int swz_nt(int r) { return (r >> 1) & 7; }
+// MN (bf16) stage swizzle: physical 32-B segment of logical segment s in K-row k
+// is s ^ swz_mn(k)
+__device__ __forceinline__ int swz_mn(int k) { return (k & 3) | ((k >> 1) & 4); }
+
+// Per-lane byte offset (relative to the stage base) of this wave's first
+// wave-wide load of one operand stage, and the byte step between its kLoads
+// loads.  Load i fills LDS bytes [(wave + 8 i) * 1024, + 1024) of the operand's
+// stage region, lane l the 16 bytes at + 16 l; the lane fetches the logical bytes
+// that belong at that physical place.  Load i covers rows (NT) or K-rows (MN)
+// 64 i, 16 i or 8 i further on, which leaves every swizzle unchanged, so one
+// offset serves all loads.
+template <typename T>
+__device__ __forceinline__ uint32_t load_offset(const Operand& op, int wave, int lane,
+                                                uint32_t& step) {
+  if (!op.mn) {
+    const int r = wave * 8 + (lane >> 3);                          // 8 rows of 128 B
+    const int c = (lane & 7) ^ swz_nt(r);
+    step = (uint32_t)(kWaves * 8 * op.ld);
+    return (uint32_t)(r * op.ld + c * 16);
+  } else if (sizeof(T) == 2) {
+    const int k = wave * 2 + (lane >> 5);                          // 2 K-rows of 512 B
+    const int pc = lane & 31;                                      // physical chunk
+    const int c = (((pc >> 1) ^ swz_mn(k)) << 1) | (pc & 1);
+    step = (uint32_t)(kWaves * 2 * op.ld);
+    return (uint32_t)(k * op.ld + c * 16);
+  } else {
+    const int k = wave;                                            // 1 K-row of 1 KB
+    step = (uint32_t)(kWaves * op.ld);
+    return (uint32_t)(k * op.ld + lane * 16);
   }
-};
+}
 
-// LDS bytes of the default pipeline.
-constexpr int kGemmLds = Pipe<kRowB, kNst>::kLds;
+// Fragment of 16 M/N indices (block origin r0 within the 256-wide tile) for K
+// sub-step ks (32 bf16 or 16 fp32 of the stage) from an operand stage region.
+// Lane l gets index r0 + (l & 15) and K elements 8 (l >> 4) .. + 7 of the
+// sub-step (bf16; fp32: 4 (l >> 4) .. + 3).
+template <typename T, bool kMN>
+__device__ __forceinline__ i32x4 read_frag(const lds_t* region, int r0, int ks, int lane) {
+  if (!kMN) {
+    const int r = r0 + (lane & 15);
+    const int c = (4 * ks + (lane >> 4)) ^ swz_nt(r);
+    return lds_read16(region + r * kStageBytes + c * 16);
+  } else if (sizeof(T) == 2) {
+    // Two transposing reads of 4 K-rows each.  Lane s of a 16-lane group points at
+    // K-row (base + s / 4), elements r0 + 4 (s % 4) .. + 3; the read hands lane j
+    // the 4 K values of element r0 + j.
+    const int g = lane >> 4, s = lane & 15;
+    const int seg = r0 >> 4;
+    const int k0 = 32 * ks + 8 * g + (s >> 2);
+    const int k1 = k0 + 4;
+    const i32x2 lo = lds_read_tr16(region + k0 * 512 + ((seg ^ swz_mn(k0)) << 5) + (s & 3) * 8);
+    const i32x2 hi = lds_read_tr16(region + k1 * 512 + ((seg ^ swz_mn(k1)) << 5) + (s & 3) * 8);
+    return i32x4{lo[0], lo[1], hi[0], hi[1]};
+  } else {
+    const int g = lane >> 4, r = r0 + (lane & 15);
+    const lds_t* p = region + (16 * ks + 4 * g) * 1024 + r * 4;
+    return i32x4{lds_read4(p), lds_read4(p + 1024), lds_read4(p + 2048), lds_read4(p + 3072)};
+  }
+}
 
-// acc[i][j] += A[m0 + wave rows] . B[n0 + wave cols]^T over k_bytes of K.
+// acc[i][j] += A(m0 + wave rows, :) . B(n0 + wave cols, :) over nk K stages.
 //
-// Stage s (ROWB bytes of K) lives in LDS buffer s % NST.  Each wave fills its
-// share of a stage with direct-to-LDS buffer loads (16 B per lane; lane l's
-// bytes land at the block base + 16 l, so the lane fetches the logical chunk
-// that belongs at that physical position of the swizzled row).  Iteration s:
-//   issue the loads of stage s + NST - 1 (into the buffer stage s - 1 used);
-//   for each 32-element sub-step: read the next fragments, run 32 MFMAs on the
-//   current ones; before the last sub-step's MFMAs, wait for stage s + 1's loads,
-//   barrier, and read stage s + 1's first fragments, so that LDS latency hides
-//   under those MFMAs.
-// The loop has no data-dependent branches: stages past the end of K are loaded
-// and read like the others (their offsets stay inside the operand, or past the
-// resource end where loads return zeros) and are never used, so every wait count
-// is a constant.  All loads are drained before returning: none may write LDS
-// after the workgroup releases it.
-template <typename T, int ROWB = kRowB, int NST = kNst>
+// Stage s lives in LDS buffer s % 2.  Each wave fills its share of a stage with
+// direct-to-LDS buffer loads.  Iteration s: for each 32-element sub-step read the
+// next fragments and run 32 MFMAs on the current ones, issuing the loads of stage
+// s + 1 (into the buffer stage s - 1 used) right after the first sub-step's reads; before the last sub-step's
+// MFMAs, wait for stage s + 1's loads, barrier, and read stage s + 1's first
+// fragments, so that LDS latency hides under those MFMAs.  The loop has no
+// data-dependent branches: the stage past the end of K is loaded (zeros or
+// unused bytes inside the operand) and read like the others and never used, so
+// every wait count is a constant.  All loads are drained before returning: none
+// may write LDS after the workgroup releases it.
+template <typename T, bool kMNA, bool kMNB>
 __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, int64_t m0,
-                                          int64_t n0, int64_t k_bytes, lds_t* lds,
+                                          int64_t n0, int nk, lds_t* lds,
                                           f32x4 (&acc)[kBI][kBJ]) {
-  typedef Pipe<ROWB, NST> P;
-  static_assert(ROWB == 128, "operand stage strides assume 128-byte stages");
-  constexpr int kLoads = kTile / P::kRowsPerLoad / kWaves;   // per wave per operand
-  constexpr int kAhead = (NST - 2) * 2 * kLoads;              // loads allowed in flight
-  static_assert(kAhead <= 63, "vmcnt range");
+  constexpr int kKs = 2;   // sub-steps per stage
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kWN, wn = wave % kWN;
 
-  const __amdgpu_buffer_rsrc_t ra = tile_rsrc(A, m0);
-  const __amdgpu_buffer_rsrc_t rb = tile_rsrc(B, n0);
-
-  // direct loads: wave-wide load i covers tile rows (wave + kWaves i) * 8 + lane / 8
-  const int lrow = wave * P::kRowsPerLoad + lane / P::kChunks;
-  const uint32_t cswz = (uint32_t)(((lane % P::kChunks) ^ P::swz(lrow)) << 4);
-  const uint32_t offA = (uint32_t)(lrow * A.ld_bytes) + cswz;
-  const uint32_t offB = (uint32_t)(lrow * B.ld_bytes) + cswz;
-  const uint32_t stepA = (uint32_t)(kWaves * P::kRowsPerLoad * A.ld_bytes);
-  const uint32_t stepB = (uint32_t)(kWaves * P::kRowsPerLoad * B.ld_bytes);
-  const uint32_t kstA = (uint32_t)A.stage_bytes, kstB = (uint32_t)B.stage_bytes;
-
-  // fragment reads: row (wave origin + 16 i + (lane & 15)), logical chunk 4 ks + (lane >> 4)
-  const int frow = lane & 15, fquad = lane >> 4;
-  const int fA = (wm * (kTile / kWM) + frow) * ROWB;
-  const int fB = kTile * ROWB + (wn * (kTile / kWN) + frow) * ROWB;
-  int fswz[P::kKs];
-#pragma unroll
-  for (int ks = 0; ks < P::kKs; ++ks) fswz[ks] = (((4 * ks + fquad) ^ P::swz(frow)) << 4);
-
-  const int nk = (int)(k_bytes / ROWB);
+  const TileRange ta = tile_range(A, m0), tb = tile_range(B, n0);
+  uint32_t stepA, stepB;
+  const uint32_t offA = load_offset<T>(A, wave, lane, stepA);
+  const uint32_t offB = load_offset<T>(B, wave, lane, stepB);
+  const int rA = wm * (kTile / kWM), rB = wn * (kTile / kWN);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
   auto issue = [&](int stage) {
-    lds_t* sa = lds + (stage % NST) * P::kStage + wave * 1024;
-    lds_t* sb = sa + kTile * ROWB;
-    const uint32_t ka = (uint32_t)stage * kstA, kb = (uint32_t)stage * kstB;
+    const uint32_t sa = lds_base + (stage & 1) * kStageLds + wave * 1024;
+    const uint32_t sb = sa + kOpLds;
+    const __amdgpu_buffer_rsrc_t ra = stage_rsrc<T>(A, ta, stage);
+    const __amdgpu_buffer_rsrc_t rb = stage_rsrc<T>(B, tb, stage);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, sa + i * kWaves * 1024, 16,
-                                               offA + i * stepA + ka, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, sb + i * kWaves * 1024, 16,
-                                               offB + i * stepB + kb, 0, 0, 0);
+      dma16(ra, offA, __builtin_amdgcn_readfirstlane(i * stepA),
+            __builtin_amdgcn_readfirstlane(sa + i * kWaves * 1024));
+      dma16(rb, offB, __builtin_amdgcn_readfirstlane(i * stepB),
+            __builtin_amdgcn_readfirstlane(sb + i * kWaves * 1024));
     }
   };
   auto read_frags = [&](i32x4 (&fa)[kBI], i32x4 (&fb)[kBJ], int stage, int ks) {
-    const lds_t* s = lds + (stage % NST) * P::kStage;
+    const lds_t* s = lds + (stage & 1) * kStageLds;
 #pragma unroll
-    for (int i = 0; i < kBI; ++i) fa[i] = lds_read16(s + fA + i * 16 * ROWB + fswz[ks]);
+    for (int i = 0; i < kBI; ++i) fa[i] = read_frag<T, kMNA>(s, rA + 16 * i, ks, lane);
 #pragma unroll
-    for (int j = 0; j < kBJ; ++j) fb[j] = lds_read16(s + fB + j * 16 * ROWB + fswz[ks]);
+    for (int j = 0; j < kBJ; ++j) fb[j] = read_frag<T, kMNB>(s + kOpLds, rB + 16 * j, ks, lane);
   };
   auto mma = [&](const i32x4 (&fa)[kBI], const i32x4 (&fb)[kBJ]) {
 #pragma unroll
@@ -220,9 +328,8 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
 
   if (nk <= 0) return;
   i32x4 fa0[kBI], fb0[kBJ], fa1[kBI], fb1[kBJ];
-#pragma unroll
-  for (int s = 0; s < NST - 1; ++s) issue(s);
-  wait_vm<kAhead>();
+  issue(0);
+  wait_vm<0>();
   pipe_barrier();
   read_frags(fa0, fb0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
@@ -230,17 +337,17 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   // sched_barrier(0) pins each phase: the next fragments' LDS reads are issued
   // before the MFMAs that consume the current ones.
   for (int kt = 0; kt < nk; ++kt) {
-    issue(kt + NST - 1);
 #pragma unroll
-    for (int ks = 0; ks < P::kKs; ++ks) {
+    for (int ks = 0; ks < kKs; ++ks) {
       i32x4(&cur_a)[kBI] = (ks & 1) ? fa1 : fa0;
       i32x4(&cur_b)[kBJ] = (ks & 1) ? fb1 : fb0;
       i32x4(&nxt_a)[kBI] = (ks & 1) ? fa0 : fa1;
       i32x4(&nxt_b)[kBJ] = (ks & 1) ? fb0 : fb1;
-      if (ks + 1 < P::kKs) {
+      if (ks + 1 < kKs) {
         read_frags(nxt_a, nxt_b, kt, ks + 1);
+        if (ks == 0) issue(kt + 1);
       } else {
-        wait_vm<kAhead>();
+        wait_vm<0>();
         pipe_barrier();
         read_frags(nxt_a, nxt_b, kt + 1, 0);
       }
@@ -254,8 +361,7 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
 }
 
 // Set every accumulator whose wave-local M row (0..127) is >= vlim to -inf.
-// Used once per tile, only on the tile holding the vocabulary's ragged end;
-// each row mask serves the four column blocks and dies.
+// Used once per tile, only on the tile holding the vocabulary's ragged end.
 __device__ __forceinline__ void mask_rows(f32x4 (&acc)[kBI][kBJ], int vlim) {
   const int q = (threadIdx.x & 63) >> 4;
 #pragma unroll

@@ -112,11 +112,7 @@ gh::WsLayout layout(const grpo_head_params* p, bool with_gemm = true) {
   off = 0;
   L.bflags = take(64);
   L.gl = take((size_t)chunk * 8);
-  const int64_t Dp = gh::ceil_div(D, 256) * 256;   // panel rows of W^T and H^T
-  L.wt = take((size_t)Dp * L.v_k * esz);
-  L.ht = take((size_t)Dp * chunk * esz);
-  L.dz = take((size_t)chunk * L.v_k * esz);
-  L.dzt = take((size_t)L.v_k * chunk * esz);
+  L.dz = take((size_t)chunk * L.v_k * esz);   // dlogits of one chunk, v-tiled
   L.bwd_bytes = off > L.fwd_bytes ? off : L.fwd_bytes;
   return L;
 }

@@ -20,10 +20,10 @@ struct WsLayout {
   size_t partials = 0, zy = 0, seq_L = 0, seq_F = 0, seq_G = 0, scal = 0, flags = 0;
   size_t fwd_bytes = 0;
   // backward (reuses the workspace from offset 0)
-  size_t bflags = 0, gl = 0, wt = 0, ht = 0, dz = 0, dzt = 0;
+  size_t bflags = 0, gl = 0, dz = 0;
   size_t bwd_bytes = 0;
   int64_t n_vt = 0;        // vocabulary tiles covering [0, v_real)
-  int64_t v_k = 0;         // n_vt * 256: vocabulary extent of the staging buffers
+  int64_t v_k = 0;         // n_vt * 256: vocabulary extent of the dlogits buffer
   int64_t chunk = 0;       // tokens per backward chunk (multiple of 256)
 };
 
@@ -46,7 +46,7 @@ struct TargetArgs {
   int mode;
   float* zy;
   const float* lse; const float* coef; const float* grad_output;
-  void* dz; int64_t v_k;
+  void* dz; int64_t dz_rows;   // dlogits buffer (v-tiled, dz_rows rows per group)
 };
 struct MergeArgs {
   const float2* partials; const float* zy; const int64_t* y; const uint8_t* mask;

@@ -51,10 +51,10 @@ def test_workspace_sizes():
     full = gb.workspace_size(p)
     # partials: 16 tiles x 1024 tokens x 8 B dominate the forward workspace
     assert fwd >= 16 * 1024 * 8
-    # backward: W^T + H^T chunk + dlogits + its transpose, bf16
-    assert full >= (1024 * 4096 + 1024 * 1024 + 2 * 1024 * 4096) * 2
+    # backward: the chunk's dlogits over the padded vocabulary, bf16
+    assert full >= 1024 * 4096 * 2
     assert full >= fwd
-    # fp32 path doubles the staging buffers
+    # fp32 path doubles the dlogits buffer
     assert gb.workspace_size(P(dtype="f32")) > full
     # chunking bounds the backward workspace
     assert gb.workspace_size(P(chunk_tokens=256)) < full
