@@ -139,7 +139,8 @@ typedef struct grpo_head_params {
 size_t grpo_head_fwd_workspace_size(const grpo_head_params* p);
 
 /* Bytes of device workspace grpo_head_bwd needs (the bf16 or fp32 dlogits of one
- * token chunk over the 256-padded vocabulary, and per-token scalars); also at
+ * token chunk over the 256-padded vocabulary, the chunk's hidden states
+ * transposed, and per-token scalars); also at
  * least grpo_head_fwd_workspace_size(p), so one buffer serves all calls.
  * 0 if p is invalid. */
 size_t grpo_head_workspace_size(const grpo_head_params* p);
@@ -213,8 +214,8 @@ size_t gspo_segment_workspace_size(const grpo_head_params* p);
  *   grpo_head_bwd: [4] at entry, [5] just before a token chunk's dlogits tile
  *                  launch (after the per-token prep),
  *                  [6] after that launch, [7] after the target-element fix-up,
- *                  [8] after the dH product, [9] just before the dW product,
- *                  [10] after it (with several chunks, [5]-[10] describe the
+ *                  [8] after the dH product, [9] after the chunk's H transpose,
+ *                  just before the dW product, [10] after it (with several chunks, [5]-[10] describe the
  *                  last one).
  * So [0]-[1], [5]-[6], [7]-[8] and [9]-[10] each bracket one matrix-core launch.
  * Returns GRPO_HEAD_INVALID_ARGUMENT if n_events < 0 or > 16. */

@@ -12,13 +12,19 @@
 //                           even, on the bf16 path; fp32 on the fp32 path)
 //      target_logit_kernel: rewrites dz[t][y_t] = g_t (1 - p_t,y_t)
 //   3. product_kernel<0>  : dH[t][d] = sum_v dz[t][v] W[v][d]
-//   4. product_kernel<1>  : dW[v][d] (+)= sum_t dz[t][v] H[t][d]
-// The products read W, H and dz where they are: W and H are MN-contiguous operands
-// (K = vocabulary rows or token rows, d contiguous), dz is K-contiguous in the dH
-// product and MN-contiguous in the dW product; the tile core forms transposed
-// fragments in LDS, so nothing is transposed in memory.  dz is stored "v-tiled":
-// [vocabulary / 256][chunk rows][256], so a 256x256 dlogits tile is one contiguous
-// 128 KB block (bf16) and either product streams it in large contiguous runs.
+//      (M = t: dz K-contiguous; N = d: W read MN-contiguous)
+//   4. transpose_kernel   : HT[d][t] of the chunk (small: D x chunk)
+//   5. product_kernel<1>  : dW[v][d] (+)= sum_t HT[d][t] dz[t][v]
+//      (M = d: HT K-contiguous; N = v: dz read MN-contiguous)
+// W and dz are read where they are; the tile core forms the transposed MFMA
+// fragments of the MN-contiguous operand with the gfx950 transposing LDS read,
+// which delivers about half the bandwidth of a plain read, so each product keeps
+// exactly one such operand, on the side with the smaller per-wave fragment count.
+// dz is stored "v-tiled": [vocabulary / 256][chunk rows][256], so a 256x256
+// dlogits tile is one contiguous 128 KB block (bf16) and either product streams
+// it in large contiguous runs.
+#include <type_traits>
+
 #include "gemm_tile.hpp"
 #include "launch.hpp"
 
@@ -117,21 +123,20 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
   }
 }
 
-// C[m][n] tile stored transposed as out[n][m..m+3] (4 consecutive M per lane), the
-// layout of dH[t][d] and dW[v][d].
+// Products with a K-contiguous A and an MN-contiguous B.
+//   kRole 0 (dH): C[m = t][n = d] stored row-major: out[m * ld_out + n];
+//   kRole 1 (dW): C[m = d][n = v] stored as out[n * ld_out + m .. + 3].
 struct ProductArgs {
   Operand A, B;
   int nk;                         // K stages
   float* out; int64_t ld_out;     // elements between out rows
-  int64_t m_limit;                // M extent written (d_model)
-  int64_t n_limit;                // N rows of out written
-  int64_t n_zero_from;            // out rows >= this are written as 0 (padded vocab)
+  int64_t m_limit;                // M extent written
+  int64_t n_limit;                // N extent written
+  int64_t zero_from;              // dW rows (N) >= this are written as 0 (padded vocab)
   int accumulate;                 // add to out
   int group_m;
 };
 
-// kRole 0: dH (A = W MN-contiguous, B = dz K-contiguous);
-// kRole 1: dW (A = H MN-contiguous, B = dz MN-contiguous).
 template <typename T, int kRole>
 __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int tiles_m,
                                                            int tiles_n) {
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
   f32x4 acc[kBI][kBJ];
   zero_acc(acc);
-  gemm_tile<T, true, kRole == 1>(a.A, a.B, m0, n0, a.nk, (lds_t*)lds, acc);
+  gemm_tile<T, false, true>(a.A, a.B, m0, n0, a.nk, (lds_t*)lds, acc);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWN, wn = wave % kWN;
@@ -150,17 +155,53 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
   for (int j = 0; j < kBJ; ++j) {
     const int64_t n = n0 + wn * (kTile / kWN) + j * 16 + (lane & 15);
     if (n >= a.n_limit) continue;
-    const bool zero = n >= a.n_zero_from;
-    float* rowp = a.out + n * a.ld_out;
+    if (kRole == 0) {
+      // 4 consecutive rows m, one column n: a 64-byte run per row across 16 lanes
 #pragma unroll
-    for (int i = 0; i < kBI; ++i) {
-      const int64_t m = mbase + i * 16;   // 4 consecutive M
-      if (m >= a.m_limit) continue;
-      f32x4 v = acc[i][j];
-      if (zero) v = f32x4{0.f, 0.f, 0.f, 0.f};
-      else if (a.accumulate) v += *(const f32x4*)(rowp + m);
-      __builtin_nontemporal_store(v, (f32x4*)(rowp + m));
+      for (int i = 0; i < kBI; ++i) {
+        const int64_t m = mbase + i * 16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (m + e >= a.m_limit) continue;
+          float* p = a.out + (m + e) * a.ld_out + n;
+          const float v = a.accumulate ? acc[i][j][e] + *p : acc[i][j][e];
+          __builtin_nontemporal_store(v, p);
+        }
+      }
+    } else {
+      const bool zero = n >= a.zero_from;
+      float* rowp = a.out + n * a.ld_out;
+#pragma unroll
+      for (int i = 0; i < kBI; ++i) {
+        const int64_t m = mbase + i * 16;   // 4 consecutive M
+        if (m >= a.m_limit) continue;
+        f32x4 v = acc[i][j];
+        if (zero) v = f32x4{0.f, 0.f, 0.f, 0.f};
+        else if (a.accumulate) v += *(const f32x4*)(rowp + m);
+        __builtin_nontemporal_store(v, (f32x4*)(rowp + m));
+      }
     }
+  }
+}
+
+// HT[d][t] = H[t][d] for t < rows, 0 for rows <= t < rows_pad; HT rows are
+// ld_out elements long.  64 x 64 element tiles through LDS.
+template <typename E>
+__global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ H, int64_t d_model,
+                                                        int64_t rows, E* __restrict__ HT,
+                                                        int64_t ld_out, int tiles_d) {
+  __shared__ E tile[64][65];
+  const int64_t td = blockIdx.x % tiles_d, tt = blockIdx.x / tiles_d;
+  const int64_t d0 = td * 64, t0 = tt * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int k = ty; k < 64; k += 4) {
+    const int64_t t = t0 + k, d = d0 + tx;
+    tile[k][tx] = (t < rows && d < d_model) ? H[t * d_model + d] : E(0);
+  }
+  __syncthreads();
+  for (int k = ty; k < 64; k += 4) {
+    const int64_t d = d0 + k, t = t0 + tx;
+    if (d < d_model) HT[d * ld_out + t] = tile[tx][k];
   }
 }
 
@@ -186,6 +227,7 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   const int64_t esz = sizeof(T);
   const int64_t N = a.n_tokens, D = a.d_model, VK = L.v_k, R = L.chunk;
   char* dz = a.ws + L.dz;
+  char* ht = a.ws + L.ht;
   float2* gl = (float2*)(a.ws + L.gl);
 
   // padded vocabulary rows of dW that no tile reaches
@@ -221,19 +263,24 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     if (e0 != hipSuccess) return e0;
     ev.mark(7, s);
 
-    // dH rows of the chunk: M = d (W read MN-contiguous), N = t (dz rows), K = v.
+    // dH rows of the chunk: M = t (dz rows), N = d (W read MN-contiguous), K = v.
     // W rows >= v_real are never read (they load as zeros).
-    ProductArgs ph{mn_row_major(a.W, D * esz, a.v_real, D, esz),
-                   nt_vtiled(dz, R, esz, (int64_t)tiles_v * R * 256 * esz),
-                   (int)(VK * esz / kStageBytes), a.dH + c0 * D, D, D, nc, INT64_MAX, 0,
-                   a.group_dh};
-    hipLaunchKernelGGL((product_kernel<T, 0>), dim3(tiles_d * tiles_t), dim3(kThreads), 0, s, ph,
-                       tiles_d, tiles_t);
+    ProductArgs ph{nt_vtiled(dz, R, esz, (int64_t)tiles_v * R * 256 * esz),
+                   mn_row_major(a.W, D * esz, a.v_real, D, esz), (int)(VK * esz / kStageBytes),
+                   a.dH + c0 * D, D, nc, D, INT64_MAX, 0, a.group_dh};
+    hipLaunchKernelGGL((product_kernel<T, 0>), dim3(tiles_t * tiles_d), dim3(kThreads), 0, s, ph,
+                       tiles_t, tiles_d);
     ev.mark(8, s);
+
+    // HT of the chunk: D rows of ncp tokens (zero past nc)
+    typedef typename std::conditional<sizeof(T) == 2, uint16_t, float>::type E;
+    const int ttd = (int)ceil_div(D, 64);
+    hipLaunchKernelGGL(transpose_kernel<E>, dim3((unsigned)(ttd * (ncp / 64))), dim3(256), 0, s,
+                       (const E*)Hc, D, nc, (E*)ht, R, ttd);
     ev.mark(9, s);
 
-    // dW: M = d (H chunk read MN-contiguous), N = v (dz read MN-contiguous), K = t
-    ProductArgs pw{mn_row_major(Hc, D * esz, nc, D, esz), mn_vtiled(dz, R, esz, tiles_v),
+    // dW: M = d (HT K-contiguous), N = v (dz read MN-contiguous), K = t
+    ProductArgs pw{nt_row_major(ht, R * esz, D), mn_vtiled(dz, R, esz, tiles_v),
                    (int)(ncp * esz / kStageBytes), a.dW, D, D, (a.v_rows < VK ? a.v_rows : VK),
                    a.v_real, c0 > 0 ? 1 : 0, a.group_dw};
     hipLaunchKernelGGL((product_kernel<T, 1>), dim3(tiles_d * tiles_v), dim3(kThreads), 0, s, pw,

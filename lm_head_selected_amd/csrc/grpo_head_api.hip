@@ -113,6 +113,7 @@ gh::WsLayout layout(const grpo_head_params* p, bool with_gemm = true) {
   L.bflags = take(64);
   L.gl = take((size_t)chunk * 8);
   L.dz = take((size_t)chunk * L.v_k * esz);   // dlogits of one chunk, v-tiled
+  L.ht = take((size_t)D * chunk * esz);       // the chunk's H transposed
   L.bwd_bytes = off > L.fwd_bytes ? off : L.fwd_bytes;
   return L;
 }

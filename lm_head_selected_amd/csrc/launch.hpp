@@ -20,7 +20,7 @@ struct WsLayout {
   size_t partials = 0, zy = 0, seq_L = 0, seq_F = 0, seq_G = 0, scal = 0, flags = 0;
   size_t fwd_bytes = 0;
   // backward (reuses the workspace from offset 0)
-  size_t bflags = 0, gl = 0, dz = 0;
+  size_t bflags = 0, gl = 0, dz = 0, ht = 0;
   size_t bwd_bytes = 0;
   int64_t n_vt = 0;        // vocabulary tiles covering [0, v_real)
   int64_t v_k = 0;         // n_vt * 256: vocabulary extent of the dlogits buffer
