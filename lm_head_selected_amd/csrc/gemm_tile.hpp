@@ -273,20 +273,21 @@ __device__ __forceinline__ i32x4 read_frag(const lds_t* region, int r0, int ks, 
 // acc[i][j] += A(m0 + wave rows, :) . B(n0 + wave cols, :) over nk K stages.
 //
 // Stage s lives in LDS buffer s % 2.  Each wave fills its share of a stage with
-// direct-to-LDS buffer loads.  Iteration s: for each 32-element sub-step read the
-// next fragments and run 32 MFMAs on the current ones, issuing the loads of stage
-// s + 1 (into the buffer stage s - 1 used) right after the first sub-step's reads; before the last sub-step's
-// MFMAs, wait for stage s + 1's loads, barrier, and read stage s + 1's first
-// fragments, so that LDS latency hides under those MFMAs.  The loop has no
-// data-dependent branches: the stage past the end of K is loaded (zeros or
-// unused bytes inside the operand) and read like the others and never used, so
-// every wait count is a constant.  All loads are drained before returning: none
-// may write LDS after the workgroup releases it.
+// direct-to-LDS buffer loads.  A stage is two 32-element sub-steps of 32 MFMAs
+// per wave.  Iteration s: read stage s's second fragments and multiply its first;
+// then wait for stage s + 1's loads and barrier -- after which every wave holds
+// all of stage s in registers, so stage s's buffer can take the loads of stage
+// s + 2, a full stage ahead of their use -- read stage s + 1's first fragments
+// and multiply stage s's second.  The next fragments' LDS reads always run
+// under the current MFMAs, one read between consecutive MFMAs.  The loop has no data-dependent branches: the stages
+// past the end of K are loaded (zeros or unused bytes inside the operand) and
+// read like the others and never used, so every wait count is a constant.  All
+// loads are drained before returning: none may write LDS after the workgroup
+// releases it.
 template <typename T, bool kMNA, bool kMNB>
 __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, int64_t m0,
                                           int64_t n0, int nk, lds_t* lds,
                                           f32x4 (&acc)[kBI][kBJ]) {
-  constexpr int kKs = 2;   // sub-steps per stage
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -329,32 +330,39 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   if (nk <= 0) return;
   i32x4 fa0[kBI], fb0[kBJ], fa1[kBI], fb1[kBJ];
   issue(0);
-  wait_vm<0>();
+  issue(1);
+  wait_vm<2 * kLoads>();   // stage 0 landed; stage 1 may still be in flight
   pipe_barrier();
   read_frags(fa0, fb0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
 
-  // sched_barrier(0) pins each phase: the next fragments' LDS reads are issued
-  // before the MFMAs that consume the current ones.
-  for (int kt = 0; kt < nk; ++kt) {
+  // Spread a phase's fragment reads over its MFMAs (one read, then one MFMA):
+  // issued as one burst, the returning LDS data stalls MFMA issue.
+  auto interleave = [&]() {
 #pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
-      i32x4(&cur_a)[kBI] = (ks & 1) ? fa1 : fa0;
-      i32x4(&cur_b)[kBJ] = (ks & 1) ? fb1 : fb0;
-      i32x4(&nxt_a)[kBI] = (ks & 1) ? fa0 : fa1;
-      i32x4(&nxt_b)[kBJ] = (ks & 1) ? fb0 : fb1;
-      if (ks + 1 < kKs) {
-        read_frags(nxt_a, nxt_b, kt, ks + 1);
-        if (ks == 0) issue(kt + 1);
-      } else {
-        wait_vm<0>();
-        pipe_barrier();
-        read_frags(nxt_a, nxt_b, kt + 1, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      mma(cur_a, cur_b);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < kBI + kBJ; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, kBI * kBJ - (kBI + kBJ), 0);
+  };
+  for (int kt = 0; kt < nk; ++kt) {
+    // sub-step 0: read stage kt's second fragments, multiply its first
+    read_frags(fa1, fb1, kt, 1);
+    mma(fa0, fb0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step 1: once every wave holds all of stage kt (its reads are drained) and
+    // stage kt + 1 has landed, stage kt's buffer takes the loads of stage kt + 2,
+    // a full stage ahead of their use
+    wait_vm<0>();
+    pipe_barrier();
+    issue(kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(fa0, fb0, kt + 1, 0);
+    mma(fa1, fb1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
   }
   wait_vm<0>();
   pipe_barrier();
