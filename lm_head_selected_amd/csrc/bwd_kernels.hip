@@ -101,8 +101,12 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
   const float c2 = a.inv_tau * kLog2e;
   // (g, lse2) of the lane's token columns; tokens past the chunk read zeros
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gl, (uint32_t)(a.chunk_tokens * 8));
-  // this tile's block of dz: rows t0 .. t0 + 255 of vocabulary group tm
+  // this tile's block of dz: rows t0 .. t0 + 255 of vocabulary group tm, one
+  // contiguous [256][256] block
   char* tile = (char*)a.dz + vtiled_offset(t0, v0, a.dz_rows, esz);
+  // bf16: the block is staged in LDS (now free) and written out as whole rows;
+  // 32-byte segment s of LDS row t sits at segment s ^ (t & 15)
+  char* L = lds;
 
 #pragma unroll
   for (int j = 0; j < kBJ; ++j) {
@@ -118,7 +122,27 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
       float d[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) d[e] = -g * fast_exp2(acc[i][j][e] * c2 - lse2);
-      Store4<T>::run(rowp + (vl + i * 16) * esz, d[0], d[1], d[2], d[3]);   // 4 consecutive v
+      const int v = vl + i * 16;                                 // 4 consecutive v
+      if (sizeof(T) == 2) {
+        const bf16x4 q = {(__bf16)d[0], (__bf16)d[1], (__bf16)d[2], (__bf16)d[3]};
+        const int byte = v * 2;                                  // within the 512-B row
+        const int seg = (byte >> 5) ^ (tl & 15);
+        *(i32x2*)(L + tl * 512 + seg * 32 + (byte & 31)) = __builtin_bit_cast(i32x2, q);
+      } else {
+        Store4<T>::run(rowp + v * esz, d[0], d[1], d[2], d[3]);
+      }
+    }
+  }
+  if (sizeof(T) == 2) {
+    __syncthreads();
+    // 256 rows x 32 chunks of 16 B, row-major: one wave writes two whole rows
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = q * kThreads + threadIdx.x;
+      const int t = idx >> 5, c = idx & 31;
+      const int seg = (c >> 1) ^ (t & 15);
+      const i32x4 v = *(const i32x4*)(L + t * 512 + seg * 32 + (c & 1) * 16);
+      __builtin_nontemporal_store(v, (i32x4*)(tile + (int64_t)t * 512 + c * 16));
     }
   }
 }
@@ -154,8 +178,8 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
 #pragma unroll
   for (int j = 0; j < kBJ; ++j) {
     const int64_t n = n0 + wn * (kTile / kWN) + j * 16 + (lane & 15);
-    if (n >= a.n_limit) continue;
     if (kRole == 0) {
+      if (n >= a.n_limit) continue;
       // 4 consecutive rows m, one column n: a 64-byte run per row across 16 lanes
 #pragma unroll
       for (int i = 0; i < kBI; ++i) {
@@ -168,18 +192,40 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
           __builtin_nontemporal_store(v, p);
         }
       }
-    } else {
-      const bool zero = n >= a.zero_from;
-      float* rowp = a.out + n * a.ld_out;
+    }
+  }
+  if (kRole == 1) {
+    // dW rows n0 .. n0 + 255, columns m0 .. m0 + 255: staged through LDS (free
+    // now) in two halves of 128 rows, then written as whole 1 KB row segments.
+    // 16-byte chunk c of LDS row r sits at chunk c ^ (r & 15).
+    float* L = (float*)lds;   // [128][256]
 #pragma unroll
-      for (int i = 0; i < kBI; ++i) {
-        const int64_t m = mbase + i * 16;   // 4 consecutive M
-        if (m >= a.m_limit) continue;
-        f32x4 v = acc[i][j];
-        if (zero) v = f32x4{0.f, 0.f, 0.f, 0.f};
-        else if (a.accumulate) v += *(const f32x4*)(rowp + m);
-        __builtin_nontemporal_store(v, (f32x4*)(rowp + m));
+    for (int p = 0; p < 2; ++p) {
+      if ((wn >> 1) == p) {
+#pragma unroll
+        for (int j = 0; j < kBJ; ++j) {
+          const int r = (wn & 1) * 64 + j * 16 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < kBI; ++i) {
+            const int c = (wm * 128 + i * 16 + (lane >> 4) * 4) >> 2;
+            *(f32x4*)(L + r * 256 + ((c ^ (r & 15)) << 2)) = acc[i][j];
+          }
+        }
       }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int r = (threadIdx.x >> 6) + 8 * q, c = threadIdx.x & 63;
+        const int64_t n = n0 + p * 128 + r, m = m0 + c * 4;
+        if (n < a.n_limit && m < a.m_limit) {
+          f32x4 v = *(const f32x4*)(L + r * 256 + ((c ^ (r & 15)) << 2));
+          float* o = a.out + n * a.ld_out + m;
+          if (n >= a.zero_from) v = f32x4{0.f, 0.f, 0.f, 0.f};
+          else if (a.accumulate) v += *(const f32x4*)o;
+          __builtin_nontemporal_store(v, (f32x4*)o);
+        }
+      }
+      __syncthreads();
     }
   }
 }
