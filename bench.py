@@ -235,9 +235,8 @@ def main():
     per_step = [hev.elapsed_ms(evs[k][0], evs[k][gb.N_STAGE_EVENTS - 1]) for k in range(K)]
     hev.destroy()
 
-    # algorithmic flops of each matrix-core launch: 2 N D x (real vocabulary rows it covers)
-    full_rows = (V // 256) * 256 if V % 256 else V
-    launch_flops = {"fwd_tiles": 2.0 * N * D * full_rows, "bwd_dlogits": 2.0 * N * D * V,
+    # algorithmic flops of each matrix-core launch: 2 N D V (real vocabulary rows)
+    launch_flops = {"fwd_tiles": 2.0 * N * D * V, "bwd_dlogits": 2.0 * N * D * V,
                     "bwd_dh": 2.0 * N * D * V, "bwd_dw": 2.0 * N * D * V}
     gemm = {s: {"ms": round(stages[s], 3),
                 "tflops": round(launch_flops[s] / (stages[s] / 1e3) / 1e12, 1)}

@@ -208,9 +208,9 @@ size_t gspo_segment_workspace_size(const grpo_head_params* p);
  * hipEvent_t handles (cast to void*; NULL entries are skipped), or events == NULL
  * to switch timing off.  The array is copied.  While set, the calls record
  * events on their stream at stage boundaries:
- *   grpo_head_fwd: [0] before the launch of the full vocabulary tiles, [1] after
- *                  it, [2] after the ragged-end tile, the target-logit gather
- *                  and the merge, [3] after the objective stage;
+ *   grpo_head_fwd: [0] before the vocabulary-tile launch, [1] after it, [2]
+ *                  after the target-logit gather and the merge, [3] after the
+ *                  objective stage;
  *   grpo_head_bwd: [4] at entry, [5] just before a token chunk's dlogits tile
  *                  launch (after the per-token prep),
  *                  [6] after that launch, [7] after the target-element fix-up,

@@ -6,7 +6,8 @@
 // leave registers.  Padded columns (vocab >= v_real) are -inf before the partial
 // is formed, and the merge folds the partials in ascending tile order starting
 // from the identity (-inf, 0) (RL-Kernel PR #291, commit notes: ShardingSpec,
-// ReductionSpec).  Partials are kept in base-2 units: m2 = max z*log2(e) and
+// ReductionSpec): ascending within 8 consecutive runs of tiles, then the runs in
+// ascending order.  Partials are kept in base-2 units: m2 = max z*log2(e) and
 // s = sum 2^(z*log2(e) - m2), so every exponential is one v_exp_f32.
 //
 // The target logit z[t, y_t] is gathered by target_logit_kernel, one wave per
@@ -24,11 +25,11 @@ __device__ __forceinline__ bool token_active(const uint8_t* mask, const int64_t*
   return mask ? (mask[t] != 0) : (y[t] != ignore_index);
 }
 
-// kPartial: this launch covers the last vocabulary tile, whose rows >= v_real are
-// padding (their W rows load as zeros) and must count as -inf.
-template <typename T, bool kPartial>
-__global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int tm_first,
-                                                            int tiles_m, int tiles_n) {
+// The tile holding the vocabulary's ragged end masks its rows >= v_real (padding:
+// their W rows load as zeros) to -inf; the branch is uniform per workgroup.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int tiles_m,
+                                                            int tiles_n) {
   // One LDS object only: with a second __shared__ array the compiler can no longer
   // tell the direct-to-LDS loads from the fragment reads and waits for every load
   // right after issuing it.  The per-half row statistics reuse the pipeline's
@@ -38,8 +39,8 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int t
 
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, a.group_m, tm, tn);
-  tm += tm_first;
   const int64_t v0 = (int64_t)tm * kTile;   // vocabulary rows of this tile
+  const bool partial = v0 + kTile > a.v_real;
   const int64_t t0 = (int64_t)tn * kTile;   // tokens of this tile
   const int64_t esz = Elem<T>::size;
 
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int t
   const int wm = wave / kWN, wn = wave % kWN;
   const float c2 = a.inv_tau * kLog2e;
   float2(*half_stats)[kTile] = (float2(*)[kTile])lds;   // [2][kTile]
-  if (kPartial) {
+  if (partial) {
     const int64_t left = a.v_real - (v0 + wm * 128);
     mask_rows(acc, (int)(left < 0 ? 0 : (left > 128 ? 128 : left)));
   }
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int t
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
     float s = 0.0f;
-    if (!kPartial || m != -INFINITY) {
+    if (m != -INFINITY) {
 #pragma unroll
       for (int i = 0; i < kBI; ++i)
 #pragma unroll
@@ -156,22 +157,44 @@ __global__ __launch_bounds__(256) void target_logit_kernel(TargetArgs a) {
   }
 }
 
-// One thread per token: fold the n_vt partials in ascending tile order.
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= a.n_tokens) return;
+// (M, S) <- (M, S) (+) (m, s): the merge of two (max, sumexp) partials in base-2
+// units; (-inf, 0) is the identity.
+__device__ __forceinline__ void fold(float& M, float& S, float m, float s) {
+  if (m == -INFINITY) return;                 // identity partial
+  if (m > M) {
+    S = S * fast_exp2(M - m) + s;             // M = -inf on the first real partial: S * 0
+    M = m;
+  } else {
+    S = S + s * fast_exp2(m - M);
+  }
+}
+
+// Fixed-order merge of the n_vt partials of each token.  A block serves 32 tokens
+// with 8 threads each: thread g folds the tiles of the g-th of 8 consecutive runs
+// in ascending order, then one thread per token folds the 8 run results in
+// ascending order.  The order is fixed, so results are bitwise repeatable.
+constexpr int kMergeTokens = 32, kMergeRuns = 8;
+__global__ __launch_bounds__(kMergeTokens * kMergeRuns) void merge_kernel(MergeArgs a) {
+  __shared__ float2 run_ms[kMergeRuns][kMergeTokens];
+  const int tl = threadIdx.x % kMergeTokens, g = threadIdx.x / kMergeTokens;
+  const int64_t t = (int64_t)blockIdx.x * kMergeTokens + tl;
+  const int64_t per = (a.n_vt + kMergeRuns - 1) / kMergeRuns;
+  const int64_t k0 = g * per, k1 = (k0 + per < a.n_vt) ? k0 + per : a.n_vt;
   float M = -INFINITY, S = 0.0f;
-  const float2* p = a.partials + t;
-  for (int64_t k = 0; k < a.n_vt; ++k) {
-    const float2 q = p[k * a.n_tokens];
-    if (q.x == -INFINITY) continue;           // identity partial
-    if (q.x > M) {
-      S = S * fast_exp2(M - q.x) + q.y;       // M = -inf on the first real tile: S*0
-      M = q.x;
-    } else {
-      S = S + q.y * fast_exp2(q.x - M);
+  if (t < a.n_tokens) {
+    const float2* p = a.partials + t;
+    for (int64_t k = k0; k < k1; ++k) {
+      const float2 q = p[k * a.n_tokens];
+      fold(M, S, q.x, q.y);
     }
   }
+  run_ms[g][tl] = make_float2(M, S);
+  __syncthreads();
+  if (g != 0 || t >= a.n_tokens) return;
+  M = -INFINITY;
+  S = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kMergeRuns; ++r) fold(M, S, run_ms[r][tl].x, run_ms[r][tl].y);
   const float lse = (M + fast_log2(S)) * kLn2;
   a.lse[t] = lse;
   float lp = 0.0f;
@@ -185,15 +208,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 template <typename T>
 static void launch_tiles(const FwdTileArgs& a, int tiles_m, int tiles_n,
                          const StageEvents& ev, hipStream_t s) {
-  // every tile but the last is entirely inside the real vocabulary
-  const int full = (a.v_real % kTile == 0) ? tiles_m : tiles_m - 1;
-  if (full > 0)
-    hipLaunchKernelGGL((fwd_tile_kernel<T, false>), dim3(full * tiles_n), dim3(kThreads), 0, s,
-                       a, 0, full, tiles_n);
+  hipLaunchKernelGGL(fwd_tile_kernel<T>, dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,
+                     tiles_m, tiles_n);
   ev.mark(1, s);
-  if (full < tiles_m)
-    hipLaunchKernelGGL((fwd_tile_kernel<T, true>), dim3(tiles_n), dim3(kThreads), 0, s, a, full,
-                       1, tiles_n);
 }
 
 hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt,
@@ -216,7 +233,8 @@ hipError_t launch_target_logit(int dtype, const TargetArgs& a, hipStream_t s) {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
   if (a.n_tokens == 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)ceil_div(a.n_tokens, 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)ceil_div(a.n_tokens, kMergeTokens)),
+                     dim3(kMergeTokens * kMergeRuns), 0, s, a);
   return hipGetLastError();
 }
 

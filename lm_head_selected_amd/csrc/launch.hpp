@@ -89,7 +89,7 @@ struct BwdArgs {
   const StageEvents* marks;
 };
 
-// records stage event 1 between the full-tile launch and the ragged-tile launch
+// records stage event 1 after the tile launch
 hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt,
                             const StageEvents& ev, hipStream_t s);
 hipError_t launch_target_logit(int dtype, const TargetArgs& a, hipStream_t s);
