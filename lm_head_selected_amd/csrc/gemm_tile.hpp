@@ -284,7 +284,7 @@ __device__ __forceinline__ i32x4 read_frag(const lds_t* region, int r0, int ks, 
 // read like the others and never used, so every wait count is a constant.  All
 // loads are drained before returning: none may write LDS after the workgroup
 // releases it.
-template <typename T, bool kMNA, bool kMNB>
+template <typename T, bool kMNA, bool kMNB, bool kQuarters = true>
 __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, int64_t m0,
                                           int64_t n0, int nk, lds_t* lds,
                                           f32x4 (&acc)[kBI][kBJ]) {
@@ -327,6 +327,41 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
       for (int j = 0; j < kBJ; ++j) Mma<T>::run(acc[i][j], fa[i], fb[j]);
   };
 
+  // Spread a phase's fragment reads over its MFMAs, one read between consecutive
+  // MFMAs: issued as one burst, the returning LDS data stalls MFMA issue.
+  auto interleave = [&]() {
+#pragma unroll
+    for (int q = 0; q < kBI + kBJ; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kBI * kBJ - (kBI + kBJ), 0);
+  };
+  // kQuarters: a sub-step runs as four quarters of 8 MFMAs (A blocks 2c, 2c + 1 by
+  // every B block); quarter 0 reads all of the next B blocks (every quarter of
+  // the next sub-step needs them), quarter c the next A blocks 2c, 2c + 1.
+  auto quarter = [&](const i32x4 (&ca)[kBI], const i32x4 (&cb)[kBJ], i32x4 (&na)[kBI],
+                     i32x4 (&nb)[kBJ], int rstage, int rks, int c) {
+    const lds_t* s = lds + (rstage & 1) * kStageLds;
+    if (c == 0) {
+#pragma unroll
+      for (int j = 0; j < kBJ; ++j) nb[j] = read_frag<T, kMNB>(s + kOpLds, rB + 16 * j, rks, lane);
+    }
+    na[2 * c] = read_frag<T, kMNA>(s, rA + 16 * (2 * c), rks, lane);
+    na[2 * c + 1] = read_frag<T, kMNA>(s, rA + 16 * (2 * c + 1), rks, lane);
+#pragma unroll
+    for (int i = 2 * c; i < 2 * c + 2; ++i)
+#pragma unroll
+      for (int j = 0; j < kBJ; ++j) Mma<T>::run(acc[i][j], ca[i], cb[j]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  static_assert(kBI == 8 && kBJ == 4, "quarters take the 8 A blocks in pairs");
+
   if (nk <= 0) return;
   i32x4 fa0[kBI], fb0[kBJ], fa1[kBI], fb1[kBJ];
   issue(0);
@@ -336,33 +371,39 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   read_frags(fa0, fb0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
 
-  // Spread a phase's fragment reads over its MFMAs (one read, then one MFMA):
-  // issued as one burst, the returning LDS data stalls MFMA issue.
-  auto interleave = [&]() {
-#pragma unroll
-    for (int q = 0; q < kBI + kBJ; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kBI * kBJ - (kBI + kBJ), 0);
-  };
   for (int kt = 0; kt < nk; ++kt) {
     // sub-step 0: read stage kt's second fragments, multiply its first
-    read_frags(fa1, fb1, kt, 1);
-    mma(fa0, fb0);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
+    if (kQuarters) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) quarter(fa0, fb0, fa1, fb1, kt, 1, c);
+    } else {
+      read_frags(fa1, fb1, kt, 1);
+      mma(fa0, fb0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // sub-step 1: once every wave holds all of stage kt (its reads are drained) and
     // stage kt + 1 has landed, stage kt's buffer takes the loads of stage kt + 2,
     // a full stage ahead of their use
     wait_vm<0>();
     pipe_barrier();
-    issue(kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(fa0, fb0, kt + 1, 0);
-    mma(fa1, fb1);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
+    if (kQuarters) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        quarter(fa1, fb1, fa0, fb0, kt + 1, 0, c);
+        if (c == 0) {
+          issue(kt + 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+      issue(kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(fa0, fb0, kt + 1, 0);
+      mma(fa1, fb1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   wait_vm<0>();
   pipe_barrier();
