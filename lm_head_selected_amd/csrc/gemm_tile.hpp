@@ -270,21 +270,27 @@ __device__ __forceinline__ i32x4 read_frag(const lds_t* region, int r0, int ks, 
   }
 }
 
+// Load-issue modes of the tile core (see gemm_tile).
+constexpr int kIssueSolo = 1;    // waves 0-3 load both operands for all 8 waves
+constexpr int kIssueSplit = 2;   // waves 0-3 load all of B, waves 4-7 all of A
+
 // acc[i][j] += A(m0 + wave rows, :) . B(n0 + wave cols, :) over nk K stages.
 //
-// Stage s lives in LDS buffer s % 2.  Each wave fills its share of a stage with
-// direct-to-LDS buffer loads.  A stage is two 32-element sub-steps of 32 MFMAs
-// per wave.  Iteration s: read stage s's second fragments and multiply its first;
-// then wait for stage s + 1's loads and barrier -- after which every wave holds
-// all of stage s in registers, so stage s's buffer can take the loads of stage
-// s + 2, a full stage ahead of their use -- read stage s + 1's first fragments
-// and multiply stage s's second.  The next fragments' LDS reads always run
-// under the current MFMAs, one read between consecutive MFMAs.  The loop has no data-dependent branches: the stages
+// Stage s lives in LDS buffer s % 2, filled with direct-to-LDS buffer loads
+// issued by a subset of the waves (kIssue; the reason is at the issue code).  A
+// stage is two 32-element sub-steps of 32 MFMAs per wave.  Iteration s: read
+// stage s's second fragments and multiply its first; then wait for stage s + 1's
+// loads and barrier -- after which every wave holds all of stage s in registers,
+// so stage s's buffer can take the loads of stage s + 2, a full stage ahead of
+// their use -- read stage s + 1's first fragments and multiply stage s's second.
+// The next fragments' LDS reads always run under the current MFMAs, one read
+// between consecutive MFMAs.  The loop has no data-dependent branches: the stages
 // past the end of K are loaded (zeros or unused bytes inside the operand) and
 // read like the others and never used, so every wait count is a constant.  All
 // loads are drained before returning: none may write LDS after the workgroup
 // releases it.
-template <typename T, bool kMNA, bool kMNB, bool kQuarters = true>
+template <typename T, bool kMNA, bool kMNB, bool kQuarters = true,
+          int kIssue = (!kMNA && !kMNB) ? kIssueSolo : kIssueSplit>
 __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, int64_t m0,
                                           int64_t n0, int nk, lds_t* lds,
                                           f32x4 (&acc)[kBI][kBJ]) {
@@ -294,23 +300,55 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   const int wm = wave / kWN, wn = wave % kWN;
 
   const TileRange ta = tile_range(A, m0), tb = tile_range(B, n0);
-  uint32_t stepA, stepB;
-  const uint32_t offA = load_offset<T>(A, wave, lane, stepA);
-  const uint32_t offB = load_offset<T>(B, wave, lane, stepB);
   const int rA = wm * (kTile / kWM), rB = wn * (kTile / kWN);
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
+  // Load issue is uneven on purpose.  Waves w and w + 4 share a SIMD.  With both
+  // operands K-contiguous, waves 0-3 issue every load of a stage (their own and
+  // their partners'), so the partner never stalls on a load burst and keeps the
+  // SIMD's matrix core fed meanwhile.  With an MN-contiguous B that measured
+  // slower than an even share; there waves 0-3 load all of B and waves 4-7 all
+  // of A, which measured faster than both the even share and the opposite split.
+  constexpr bool kSolo = kIssue == kIssueSolo;
+  constexpr int kHalf = kWaves / 2;
+  const int lw = wave & (kHalf - 1);
+  uint32_t stepA, stepB;
+  const uint32_t offA0 = load_offset<T>(A, lw, lane, stepA);
+  const uint32_t offA1 = load_offset<T>(A, lw + kHalf, lane, stepA);
+  const uint32_t offB0 = load_offset<T>(B, lw, lane, stepB);
+  const uint32_t offB1 = load_offset<T>(B, lw + kHalf, lane, stepB);
   auto issue = [&](int stage) {
-    const uint32_t sa = lds_base + (stage & 1) * kStageLds + wave * 1024;
-    const uint32_t sb = sa + kOpLds;
-    const __amdgpu_buffer_rsrc_t ra = stage_rsrc<T>(A, ta, stage);
-    const __amdgpu_buffer_rsrc_t rb = stage_rsrc<T>(B, tb, stage);
+    const uint32_t s0 = lds_base + (stage & 1) * kStageLds + lw * 1024;
+    const uint32_t s1 = s0 + kHalf * 1024;
+    const bool first = wave < kHalf;
+    if (kSolo) {
+      if (!first) return;
+      const __amdgpu_buffer_rsrc_t ra = stage_rsrc<T>(A, ta, stage);
+      const __amdgpu_buffer_rsrc_t rb = stage_rsrc<T>(B, tb, stage);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      dma16(ra, offA, __builtin_amdgcn_readfirstlane(i * stepA),
-            __builtin_amdgcn_readfirstlane(sa + i * kWaves * 1024));
-      dma16(rb, offB, __builtin_amdgcn_readfirstlane(i * stepB),
-            __builtin_amdgcn_readfirstlane(sb + i * kWaves * 1024));
+      for (int i = 0; i < kLoads; ++i) {
+        const uint32_t ia = __builtin_amdgcn_readfirstlane(i * stepA);
+        const uint32_t ib = __builtin_amdgcn_readfirstlane(i * stepB);
+        const uint32_t l0 = __builtin_amdgcn_readfirstlane(s0 + i * kWaves * 1024);
+        const uint32_t l1 = __builtin_amdgcn_readfirstlane(s1 + i * kWaves * 1024);
+        dma16(ra, offA0, ia, l0);
+        dma16(rb, offB0, ib, l0 + kOpLds);
+        dma16(ra, offA1, ia, l1);
+        dma16(rb, offB1, ib, l1 + kOpLds);
+      }
+    } else {
+      // waves 0-3 take B, waves 4-7 take A; each loads the shares of waves lw, lw + 4
+      const __amdgpu_buffer_rsrc_t r = first ? stage_rsrc<T>(B, tb, stage)
+                                             : stage_rsrc<T>(A, ta, stage);
+      const uint32_t o0 = first ? offB0 : offA0, o1 = first ? offB1 : offA1;
+      const uint32_t step = first ? stepB : stepA;
+      const uint32_t region = first ? (uint32_t)kOpLds : 0u;
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const uint32_t is = __builtin_amdgcn_readfirstlane(i * step);
+        dma16(r, o0, is, __builtin_amdgcn_readfirstlane(s0 + region + i * kWaves * 1024));
+        dma16(r, o1, is, __builtin_amdgcn_readfirstlane(s1 + region + i * kWaves * 1024));
+      }
     }
   };
   auto read_frags = [&](i32x4 (&fa)[kBI], i32x4 (&fb)[kBJ], int stage, int ks) {
@@ -366,7 +404,7 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   i32x4 fa0[kBI], fb0[kBJ], fa1[kBI], fb1[kBJ];
   issue(0);
   issue(1);
-  wait_vm<2 * kLoads>();   // stage 0 landed; stage 1 may still be in flight
+  wait_vm<(kSolo ? 4 : 2) * kLoads>();   // stage 0 landed; stage 1 may be in flight
   pipe_barrier();
   read_frags(fa0, fb0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
