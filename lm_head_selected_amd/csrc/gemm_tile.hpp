@@ -289,7 +289,7 @@ constexpr int kIssueSplit = 2;   // waves 0-3 load all of B, waves 4-7 all of A
 // read like the others and never used, so every wait count is a constant.  All
 // loads are drained before returning: none may write LDS after the workgroup
 // releases it.
-template <typename T, bool kMNA, bool kMNB, bool kQuarters = true,
+template <typename T, bool kMNA, bool kMNB,
           int kIssue = (!kMNA && !kMNB) ? kIssueSolo : kIssueSplit>
 __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, int64_t m0,
                                           int64_t n0, int nk, lds_t* lds,
@@ -358,24 +358,7 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
 #pragma unroll
     for (int j = 0; j < kBJ; ++j) fb[j] = read_frag<T, kMNB>(s + kOpLds, rB + 16 * j, ks, lane);
   };
-  auto mma = [&](const i32x4 (&fa)[kBI], const i32x4 (&fb)[kBJ]) {
-#pragma unroll
-    for (int i = 0; i < kBI; ++i)
-#pragma unroll
-      for (int j = 0; j < kBJ; ++j) Mma<T>::run(acc[i][j], fa[i], fb[j]);
-  };
-
-  // Spread a phase's fragment reads over its MFMAs, one read between consecutive
-  // MFMAs: issued as one burst, the returning LDS data stalls MFMA issue.
-  auto interleave = [&]() {
-#pragma unroll
-    for (int q = 0; q < kBI + kBJ; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kBI * kBJ - (kBI + kBJ), 0);
-  };
-  // kQuarters: a sub-step runs as four quarters of 8 MFMAs (A blocks 2c, 2c + 1 by
+  // A sub-step runs as four quarters of 8 MFMAs (A blocks 2c, 2c + 1 by
   // every B block); quarter 0 reads all of the next B blocks (every quarter of
   // the next sub-step needs them), quarter c the next A blocks 2c, 2c + 1.
   auto quarter = [&](const i32x4 (&ca)[kBI], const i32x4 (&cb)[kBJ], i32x4 (&na)[kBI],
@@ -411,36 +394,21 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
 
   for (int kt = 0; kt < nk; ++kt) {
     // sub-step 0: read stage kt's second fragments, multiply its first
-    if (kQuarters) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) quarter(fa0, fb0, fa1, fb1, kt, 1, c);
-    } else {
-      read_frags(fa1, fb1, kt, 1);
-      mma(fa0, fb0);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    for (int c = 0; c < 4; ++c) quarter(fa0, fb0, fa1, fb1, kt, 1, c);
     // sub-step 1: once every wave holds all of stage kt (its reads are drained) and
     // stage kt + 1 has landed, stage kt's buffer takes the loads of stage kt + 2,
-    // a full stage ahead of their use
+    // a full stage ahead of their use (issued as one burst after the first quarter:
+    // spread over the quarters, or issued before them, measured slower)
     wait_vm<0>();
     pipe_barrier();
-    if (kQuarters) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        quarter(fa1, fb1, fa0, fb0, kt + 1, 0, c);
-        if (c == 0) {
-          issue(kt + 2);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+    for (int c = 0; c < 4; ++c) {
+      quarter(fa1, fb1, fa0, fb0, kt + 1, 0, c);
+      if (c == 0) {
+        issue(kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
-      issue(kt + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(fa0, fb0, kt + 1, 0);
-      mma(fa1, fb1);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
   wait_vm<0>();
