@@ -229,6 +229,27 @@ def main():
     ms_step = start.elapsed_time(end) / K
     value = N / (ms_step / 1e3)
 
+    # the forward-only selected log-prob entry (how a trainer gets the old and the
+    # reference policy's log-probs) on the same inputs, timed after the steps
+    lp_ws = torch.empty(gb.logp_workspace_size(p), dtype=torch.uint8, device=dev)
+    lp_out = torch.empty(N, dtype=torch.float32, device=dev)
+    lse_out = torch.empty(N, dtype=torch.float32, device=dev)
+
+    def logp_call():
+        gb.grpo_head_logp(p, d["H"], d["W"], d["y"], d["mask"], lp_out, lse_out, lp_ws,
+                          stream=stream)
+
+    logp_call()
+    K2 = max(3, K // 2)
+    l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    l0.record(stream)
+    for _ in range(K2):
+        logp_call()
+    l1.record(stream)
+    torch.cuda.synchronize()
+    ms_logp = l0.elapsed_time(l1) / K2
+
     stages = {}
     for name, (a, b) in gb.STAGES.items():
         stages[name] = float(np.mean([hev.elapsed_ms(evs[k][a], evs[k][b]) for k in range(K)]))
@@ -267,6 +288,9 @@ def main():
         "stages_ms": {k: round(v, 3) for k, v in stages.items()},
         "wall_s": round(wall, 3),
         "roofline": roofline,
+        "logp_entry": {"ms": round(ms_logp, 3), "calls": K2,
+                       "tokens_per_s": round(N / (ms_logp / 1e3), 1),
+                       "tflops_2nvd": round(2.0 * N * V * D / (ms_logp / 1e3) / 1e12, 1)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)

@@ -203,6 +203,32 @@ int gspo_segment_reduce(const grpo_head_params* p, const float* logp, const floa
  * scalars).  0 if p is invalid. */
 size_t gspo_segment_workspace_size(const grpo_head_params* p);
 
+/* Forward-only selected log-probs: the vocabulary-tile stage and the ordered
+ * merge of grpo_head_fwd, without the objective.  This is the one log-prob
+ * operator a trainer calls for the policy and for the reference policy (and for
+ * the old policy before an update): RL-Kernel PR #291 "Add deterministic
+ * DP-aware GRPO loss on the TP-aware logprob path", Sequence Diagram(s) (the loss
+ * asks the log-prob op for policy and reference log-probs) and the review
+ * comment on the log-prob operator's usage example (the op returns logp and
+ * lse); Liger-Kernel PR #1160 "[GRPO] add chunked grpo streaming over vocab",
+ * conversation (a forward-only selective log-prob test against a reference).
+ *   logp[t] = z[t, y_t] - lse[t] for active tokens, 0 for inactive ones;
+ *   lse[t]  = LSE over the real vocabulary, for every token.
+ * Both are bitwise equal to grpo_head_fwd's logp and lse for the same inputs.
+ * Uses p->n_tokens, d_model, v_real, v_rows, ignore_index, dtype, inv_tau and
+ * validate; every other field is ignored (n_seqs may be 0).  Needs
+ * grpo_head_logp_workspace_size(p) bytes of workspace.
+ * Status 0, 1, 2, 6; with validate also 4 (an active target outside
+ * [0, v_real)) and 5 (a non-finite lse or logp).  A batch with no active token is
+ * not an error here: logp is all zeros and lse is still written. */
+int grpo_head_logp(const grpo_head_params* p, const void* H, const void* W, const int64_t* y,
+                   const uint8_t* mask, float* logp, float* lse, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* Bytes of device workspace grpo_head_logp needs (per-tile partials and target
+ * logits).  0 if p is invalid. */
+size_t grpo_head_logp_workspace_size(const grpo_head_params* p);
+
 /* Stage timing for measurement tools; off by default, process-wide, not for
  * concurrent use from several threads.  `events` holds `n_events` caller-created
  * hipEvent_t handles (cast to void*; NULL entries are skipped), or events == NULL
@@ -210,7 +236,7 @@ size_t gspo_segment_workspace_size(const grpo_head_params* p);
  * events on their stream at stage boundaries:
  *   grpo_head_fwd: [0] before the vocabulary-tile launch, [1] after it, [2]
  *                  after the target-logit gather and the merge, [3] after the
- *                  objective stage;
+ *                  objective stage (grpo_head_logp records [0]-[2] the same way);
  *   grpo_head_bwd: [4] at entry, [5] just before a token chunk's dlogits tile
  *                  launch (after the per-token prep),
  *                  [6] after that launch, [7] after the target-element fix-up,

@@ -24,7 +24,8 @@ STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "WORKSPACE_TOO_SMALL", 3: "NO_ACTIV
 
 EXPORTS = ("grpo_head_fwd_workspace_size", "grpo_head_workspace_size",
            "gspo_segment_workspace_size", "grpo_head_fwd", "grpo_head_bwd",
-           "gspo_segment_reduce", "grpo_head_set_stage_events", "grpo_head_last_error")
+           "gspo_segment_reduce", "grpo_head_logp", "grpo_head_logp_workspace_size",
+           "grpo_head_set_stage_events", "grpo_head_last_error")
 
 # stage-event slots recorded by grpo_head_fwd / grpo_head_bwd
 N_STAGE_EVENTS = 11
@@ -61,7 +62,7 @@ def _load():
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     pp = ctypes.POINTER(Params)
     for name in ("grpo_head_fwd_workspace_size", "grpo_head_workspace_size",
-                 "gspo_segment_workspace_size"):
+                 "gspo_segment_workspace_size", "grpo_head_logp_workspace_size"):
         getattr(lib, name).argtypes = [pp]
         getattr(lib, name).restype = sz
     lib.grpo_head_fwd.argtypes = [pp] + [vp] * 13 + [vp, sz, vp]
@@ -70,6 +71,8 @@ def _load():
     lib.grpo_head_bwd.restype = i32
     lib.gspo_segment_reduce.argtypes = [pp] + [vp] * 11 + [vp, sz, vp]
     lib.gspo_segment_reduce.restype = i32
+    lib.grpo_head_logp.argtypes = [pp] + [vp] * 6 + [vp, sz, vp]
+    lib.grpo_head_logp.restype = i32
     lib.grpo_head_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     lib.grpo_head_set_stage_events.restype = i32
     lib.grpo_head_last_error.argtypes = []
@@ -138,6 +141,10 @@ def segment_workspace_size(p: Params) -> int:
     return lib.gspo_segment_workspace_size(ctypes.byref(p))
 
 
+def logp_workspace_size(p: Params) -> int:
+    return lib.grpo_head_logp_workspace_size(ctypes.byref(p))
+
+
 def grpo_head_fwd(p, H, W, y, mask, sid, adv, old_logp, ref_logp, logp, lse, out3, coef,
                   counts, ws, ws_bytes=None, stream=None):
     ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
@@ -162,6 +169,12 @@ def gspo_segment_reduce(p, logp, old_logp, ref_logp, mask, y, sid, adv, out3, co
                                    _ptr(mask), _ptr(y), _ptr(sid), _ptr(adv), _ptr(out3),
                                    _ptr(coef), _ptr(seg_mean_logp), _ptr(counts), _ptr(ws),
                                    ws_bytes, _stream(stream)))
+
+
+def grpo_head_logp(p, H, W, y, mask, logp, lse, ws, ws_bytes=None, stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(lib.grpo_head_logp(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(y), _ptr(mask), _ptr(logp),
+                              _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 class GrpoHead:

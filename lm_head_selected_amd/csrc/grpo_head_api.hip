@@ -44,6 +44,8 @@ int hip_fail(hipError_t e, const char* where) {
 // Every tile-row block of an operand is addressed with 32-bit buffer offsets.
 constexpr int64_t kMaxRowBytes = (int64_t(1) << 31) / 256 - 1;
 
+int check_gemm(const grpo_head_params* p);
+
 int check_common(const grpo_head_params* p, bool need_gemm) {
   if (!p) return fail(GRPO_HEAD_INVALID_ARGUMENT, "params is NULL");
   if (p->n_tokens < 0) return fail(GRPO_HEAD_INVALID_ARGUMENT, "n_tokens < 0");
@@ -65,6 +67,16 @@ int check_common(const grpo_head_params* p, bool need_gemm) {
   if (p->validate != 0 && p->validate != 1)
     return fail(GRPO_HEAD_INVALID_ARGUMENT, "validate must be 0 or 1");
   if (!need_gemm) return GRPO_HEAD_OK;
+  return check_gemm(p);
+}
+
+// The fields the vocabulary-tile stage uses (grpo_head_logp checks only these).
+int check_gemm(const grpo_head_params* p) {
+  if (p->n_tokens < 0) return fail(GRPO_HEAD_INVALID_ARGUMENT, "n_tokens < 0");
+  if (p->n_tokens > (int64_t(1) << 31) - 1)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "n_tokens above 2^31 - 1");
+  if (p->validate != 0 && p->validate != 1)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "validate must be 0 or 1");
   if (p->dtype != GRPO_HEAD_BF16 && p->dtype != GRPO_HEAD_F32)
     return fail(GRPO_HEAD_INVALID_ARGUMENT, "unknown dtype %d", p->dtype);
   if (p->d_model <= 0 || p->d_model % 64 != 0)
@@ -145,6 +157,37 @@ int finish_validation(uint32_t* dflags, hipStream_t s, bool check_active) {
   if (check_active && h[1] == 0) return fail(GRPO_HEAD_NO_ACTIVE_TOKENS, "no active token");
   if (h[0] & gh::kFlagNonfinite) return fail(GRPO_HEAD_NONFINITE, "non-finite value");
   return ok();
+}
+
+// The vocabulary-tile stage, the target-logit gather and the ordered merge:
+// logp and lse of every token (nothing is enqueued for an empty batch).
+int run_logp(const grpo_head_params* p, const gh::WsLayout& L, char* w, const void* H,
+             const void* W, const int64_t* y, const uint8_t* mask, float* logp, float* lse,
+             hipStream_t s) {
+  if (p->n_tokens == 0) return GRPO_HEAD_OK;
+  g_marks.mark(0, s);
+  gh::FwdTileArgs fa{W, H, p->n_tokens, p->d_model, p->v_real, p->inv_tau,
+                     (float2*)(w + L.partials),
+                     logit_group(p->n_tokens, p->d_model, p->dtype == GRPO_HEAD_F32 ? 4 : 2)};
+  hipError_t e = gh::launch_fwd_tiles(p->dtype, fa, L.n_vt, g_marks, s);
+  if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
+  gh::TargetArgs ta{H, W, y, mask, p->n_tokens, p->d_model, p->v_real, p->ignore_index,
+                    p->inv_tau, 0, (float*)(w + L.zy), nullptr, nullptr, nullptr, nullptr, 0};
+  e = gh::launch_target_logit(p->dtype, ta, s);
+  if (e != hipSuccess) return hip_fail(e, "target logit kernel");
+  gh::MergeArgs ma{(const float2*)(w + L.partials), (const float*)(w + L.zy), y, mask,
+                   p->n_tokens, L.n_vt, p->v_real, p->ignore_index, logp, lse};
+  e = gh::launch_merge(ma, s);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel");
+  g_marks.mark(2, s);
+  return GRPO_HEAD_OK;
+}
+
+// Workspace layout of grpo_head_logp: the sequence fields play no part.
+gh::WsLayout logp_layout(const grpo_head_params* p) {
+  grpo_head_params q = *p;
+  q.n_seqs = 0;
+  return layout(&q);
 }
 
 int run_loss(const grpo_head_params* p, const gh::WsLayout& L, char* ws, const float* logp,
@@ -234,23 +277,8 @@ int grpo_head_fwd(const grpo_head_params* p, const void* H, const void* W, const
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   hipError_t e;
-  if (p->n_tokens > 0) {
-    g_marks.mark(0, s);
-    gh::FwdTileArgs fa{W, H, p->n_tokens, p->d_model, p->v_real, p->inv_tau,
-                       (float2*)(w + L.partials),
-                       logit_group(p->n_tokens, p->d_model, p->dtype == GRPO_HEAD_F32 ? 4 : 2)};
-    e = gh::launch_fwd_tiles(p->dtype, fa, L.n_vt, g_marks, s);
-    if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
-    gh::TargetArgs ta{H, W, y, mask, p->n_tokens, p->d_model, p->v_real, p->ignore_index,
-                      p->inv_tau, 0, (float*)(w + L.zy), nullptr, nullptr, nullptr, nullptr, 0};
-    e = gh::launch_target_logit(p->dtype, ta, s);
-    if (e != hipSuccess) return hip_fail(e, "target logit kernel");
-    gh::MergeArgs ma{(const float2*)(w + L.partials), (const float*)(w + L.zy), y, mask,
-                     p->n_tokens, L.n_vt, p->v_real, p->ignore_index, logp, lse};
-    e = gh::launch_merge(ma, s);
-    if (e != hipSuccess) return hip_fail(e, "merge kernel");
-    g_marks.mark(2, s);
-  }
+  rc = run_logp(p, L, w, H, W, y, mask, logp, lse, s);
+  if (rc) return rc;
   rc = run_loss(p, L, w, logp, old_logp, ref_logp, mask, y, sid, adv, out3, coef, counts,
                 nullptr, s);
   if (rc) return rc;
@@ -261,6 +289,41 @@ int grpo_head_fwd(const grpo_head_params* p, const void* H, const void* W, const
     e = gh::launch_validate(va, s);
     if (e != hipSuccess) return hip_fail(e, "validation kernel");
     return finish_validation((uint32_t*)(w + L.flags), s, true);
+  }
+  return ok();
+}
+
+size_t grpo_head_logp_workspace_size(const grpo_head_params* p) {
+  if (!p) {
+    fail(GRPO_HEAD_INVALID_ARGUMENT, "params is NULL");
+    return 0;
+  }
+  if (check_gemm(p) != GRPO_HEAD_OK) return 0;
+  return logp_layout(p).fwd_bytes;
+}
+
+int grpo_head_logp(const grpo_head_params* p, const void* H, const void* W, const int64_t* y,
+                   const uint8_t* mask, float* logp, float* lse, void* ws, size_t ws_bytes,
+                   void* stream) {
+  if (!p) return fail(GRPO_HEAD_INVALID_ARGUMENT, "params is NULL");
+  int rc = check_gemm(p);
+  if (rc) return rc;
+  if (p->n_tokens > 0 && (!H || !W || !y || !logp || !lse))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "a required buffer is NULL");
+  const gh::WsLayout L = logp_layout(p);
+  if (!ws || ws_bytes < L.fwd_bytes)
+    return fail(GRPO_HEAD_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes,
+                L.fwd_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  rc = run_logp(p, L, w, H, W, y, mask, logp, lse, s);
+  if (rc) return rc;
+  if (p->validate) {
+    gh::ValidateArgs va{p->n_tokens, 0, p->v_real, p->ignore_index, y, mask, nullptr,
+                        lse, logp, nullptr, nullptr, nullptr, (uint32_t*)(w + L.flags)};
+    hipError_t e = gh::launch_validate(va, s);
+    if (e != hipSuccess) return hip_fail(e, "validation kernel");
+    return finish_validation((uint32_t*)(w + L.flags), s, false);
   }
   return ok();
 }

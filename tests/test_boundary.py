@@ -116,3 +116,33 @@ def test_segment_reduce_needs_targets_without_mask():
         gb.gspo_segment_reduce(q, 1, 1, None, None, None, 1, 1, 1, 1, None, 1, 1,
                                ws_bytes=1 << 30, stream=0)
     assert e.value.status == 1 and "mask" in str(e.value)
+
+
+def test_logp_entry_checks_only_its_fields():
+    # the objective and sequence fields play no part in the forward-only log-probs
+    junk = P(n_seqs=0, eps_low=5.0, beta=-1.0, reduction=9, level=7)
+    size = gb.logp_workspace_size(junk)
+    assert size >= 16 * 1024 * 8                      # the per-tile partials
+    assert size == gb.logp_workspace_size(P(n_seqs=3))
+    assert size <= gb.fwd_workspace_size(P())
+    for bad in (dict(d_model=100), dict(v_real=0), dict(v_rows=10), dict(dtype=7),
+                dict(inv_tau=0.0), dict(n_tokens=-1)):
+        p = P(**bad)
+        assert gb.logp_workspace_size(p) == 0
+        with pytest.raises(gb.GrpoHeadError) as e:
+            gb.grpo_head_logp(p, 1, 1, 1, None, 1, 1, 1, ws_bytes=1 << 40, stream=0)
+        assert e.value.status == 1
+
+
+def test_logp_entry_rejects_null_buffers_and_small_workspace():
+    p = P()
+    with pytest.raises(gb.GrpoHeadError) as e:   # y NULL
+        gb.grpo_head_logp(p, 1, 1, None, 1, 1, 1, 1, ws_bytes=1 << 40, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(gb.GrpoHeadError) as e:   # lse NULL
+        gb.grpo_head_logp(p, 1, 1, 1, None, 1, None, 1, ws_bytes=1 << 40, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(gb.GrpoHeadError) as e:
+        gb.grpo_head_logp(p, 1, 1, 1, None, 1, 1, 1, ws_bytes=gb.logp_workspace_size(p) - 1,
+                          stream=0)
+    assert e.value.status == 2
