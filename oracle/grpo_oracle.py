@@ -24,9 +24,10 @@ Sources of each step (page title, section):
     hold ``ignore_index``: same page, commit notes (MaskMode).
   * the objective acts per token / per sequence; the loss triple
     (loss, policy_loss, kl); token normalisers ``global_active_tokens`` (masked
-    mean) and ``per_sequence_then_mean`` counting only sequences with active
-    tokens; no division by zero for an empty batch: same page, Overview / Key
-    Changes and the zero-active-token review thread.
+    mean), ``per_sequence_then_mean`` counting only sequences with active
+    tokens, and ``fixed_constant`` (Dr. GRPO); no division by zero for an empty
+    batch: same page, Overview / Key Changes and the zero-active-token review
+    thread.
   * softmax recovered from the logits and the LSE for the backward: same page,
     review thread on the saved fp32 logits.
   * GSPO: per-token contributions aggregated per segment with ``index_add``, then
@@ -158,14 +159,22 @@ def sequence_counts(sid, active, n_seqs: int) -> np.ndarray:
     return L
 
 
-def _weights(sid, active, L, reduction: str) -> np.ndarray:
+def _weights(sid, active, L, reduction: str, norm_const=None) -> np.ndarray:
     """Token weights of the loss normaliser (RL-Kernel PR #291, Key Changes,
     LossReductionSpec.token_normalizer):
-      token_mean    (global_active_tokens, the masked mean): w_t = m_t / T_act
-      sequence_mean (per_sequence_then_mean):  w_t = m_t / (L_{s(t)} * S_live),
-                     S_live counting only sequences with at least one active token.
+      token_mean     (global_active_tokens, the masked mean): w_t = m_t / T_act
+      sequence_mean  (per_sequence_then_mean):  w_t = m_t / (L_{s(t)} * S_live),
+                      S_live counting only sequences with at least one active token.
+      fixed_constant (Dr. GRPO): w_t = m_t / C for the caller's constant C > 0.
+                      The page names this normaliser without fixing C; reading: C
+                      is an input.
     An empty batch gives all-zero weights (no division by zero)."""
     w = np.zeros(len(sid))
+    if reduction == "fixed_constant":
+        if norm_const is None or not norm_const > 0:
+            raise ValueError("fixed_constant needs norm_const > 0")
+        w[active] = 1.0 / float(norm_const)
+        return w
     T_act = int(active.sum())
     if T_act == 0:
         return w
@@ -187,7 +196,7 @@ def _k3(logp, ref):
 
 
 def grpo_objective(logp, old, ref, adv, sid, active, n_seqs: int, eps_low: float,
-                   eps_high: float, beta: float, reduction: str) -> dict:
+                   eps_high: float, beta: float, reduction: str, norm_const=None) -> dict:
     """Token-level GRPO clipped objective with k3 KL.
 
     Per token (the objective is elementwise, RL-Kernel PR #291 Overview):
@@ -201,7 +210,7 @@ def grpo_objective(logp, old, ref, adv, sid, active, n_seqs: int, eps_low: float
     sid = np.asarray(sid)
     logp = np.asarray(logp, np.float64)
     L = sequence_counts(sid, active, n_seqs)
-    w = _weights(sid, active, L, reduction)
+    w = _weights(sid, active, L, reduction, norm_const)
     old = np.where(active, np.asarray(old, np.float64), logp)   # inactive: never read
     a = np.asarray(adv, np.float64)[sid]
     r = np.exp(logp - old)
@@ -281,7 +290,7 @@ def objective(inp: dict, logp) -> dict:
                               active, inp["n_seqs"], inp["eps_low"], inp["eps_high"], inp["beta"])
     return grpo_objective(logp, inp["old_logp"], inp["ref_logp"], inp["adv"], inp["sid"], active,
                           inp["n_seqs"], inp["eps_low"], inp["eps_high"], inp["beta"],
-                          inp["reduction"])
+                          inp["reduction"], inp.get("norm_const"))
 
 
 # ---------------------------------------------------------------------------

@@ -158,6 +158,7 @@ def _fd(f, x, h):
 
 
 @pytest.mark.parametrize("level,reduction,beta", [("token", "token_mean", 0.04),
+                                                   ("token", "fixed_constant", 0.06),
                                                    ("token", "sequence_mean", 0.1),
                                                    ("sequence_gspo", "sequence_mean", 0.07)])
 def test_coef_is_the_logp_derivative(level, reduction, beta):
@@ -181,7 +182,8 @@ def test_coef_is_the_logp_derivative(level, reduction, beta):
 
     def run(lp):
         if level == "token":
-            return oracle.grpo_objective(lp, old, ref, adv, sid, act, 4, *eps, beta, reduction)
+            return oracle.grpo_objective(lp, old, ref, adv, sid, act, 4, *eps, beta, reduction,
+                                         norm_const=37.5)
         return oracle.gspo_objective(lp, old, ref, adv, sid, act, 4, *eps, beta)
 
     out = run(logp0)
@@ -196,3 +198,38 @@ def test_coef_is_the_logp_derivative(level, reduction, beta):
             return run(lp)["loss"]
         d = _fd(f, np.array([logp0[t]]), 1e-6)
         assert d == pytest.approx(out["coef"][t], rel=1e-6, abs=1e-10), t
+
+
+def test_fixed_constant_at_the_active_count_is_the_token_mean():
+    """fixed_constant divides the active-token sums by the caller's C; at
+    C = T_act it is the masked token mean exactly, and the result scales as 1/C."""
+    g = np.random.default_rng(5)
+    lens = [4, 7, 3]
+    sid, act, adv, logp = _batch(lens, [1, 5, 12])
+    old = logp + g.standard_normal(len(sid)) * 0.3
+    ref = logp + g.standard_normal(len(sid)) * 0.2
+    T = int(act.sum())
+    tm = oracle.grpo_objective(logp, old, ref, adv, sid, act, 3, .2, .28, .1, "token_mean")
+    fc = oracle.grpo_objective(logp, old, ref, adv, sid, act, 3, .2, .28, .1, "fixed_constant",
+                               norm_const=T)
+    for k in ("loss", "policy_loss", "kl"):
+        assert fc[k] == pytest.approx(tm[k], rel=1e-14)
+    np.testing.assert_allclose(fc["coef"], tm["coef"], rtol=1e-14)
+    big = oracle.grpo_objective(logp, old, ref, adv, sid, act, 3, .2, .28, .1, "fixed_constant",
+                                norm_const=4.0 * T)
+    for k in ("loss", "policy_loss", "kl"):
+        assert big[k] == pytest.approx(tm[k] / 4.0, rel=1e-14)
+    np.testing.assert_allclose(big["coef"], tm["coef"] / 4.0, rtol=1e-14)
+    # sequences weigh by their token count, unlike sequence_mean
+    sm = oracle.grpo_objective(logp, old, ref, adv, sid, act, 3, .2, .28, .1, "sequence_mean")
+    assert abs(sm["policy_loss"] - tm["policy_loss"]) > 1e-6
+
+
+def test_fixed_constant_empty_batch_and_bad_constant():
+    sid, act, adv, logp = _batch([3, 2], [0, 1, 2, 3, 4])
+    out = oracle.grpo_objective(logp, logp, logp, adv, sid, act, 2, .2, .2, .1,
+                                "fixed_constant", norm_const=64.0)
+    assert (out["loss"], out["policy_loss"], out["kl"]) == (0.0, 0.0, 0.0)
+    assert np.all(out["coef"] == 0)
+    with pytest.raises(ValueError):
+        oracle.grpo_objective(logp, logp, logp, adv, sid, act, 2, .2, .2, .1, "fixed_constant")
