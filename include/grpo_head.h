@@ -59,8 +59,8 @@
  *   sid [n_tokens] int32 sequence / segment id, non-decreasing, in [0, n_seqs);
  *   adv [n_seqs] fp32 advantage per sequence / segment;
  *   old_logp, ref_logp, logp, lse, coef [n_tokens] fp32; counts [n_seqs] int32;
- *   out3 [3] fp32 = {loss, policy_loss, kl}; dH [n_tokens][d_model] fp32;
- *   dW [v_rows][d_model] fp32.
+ *   out3 [3] fp32 = {loss, policy_loss, kl}; dH [n_tokens][d_model] and
+ *   dW [v_rows][d_model] fp32, or bf16 with p->grad_dtype = GRPO_HEAD_GRAD_BF16.
  */
 #ifndef GRPO_HEAD_H
 #define GRPO_HEAD_H
@@ -86,7 +86,9 @@ typedef enum grpo_head_status {
 } grpo_head_status;
 
 enum { GRPO_HEAD_BF16 = 0, GRPO_HEAD_F32 = 1 };                  /* p->dtype */
-enum { GRPO_HEAD_TOKEN_MEAN = 0, GRPO_HEAD_SEQUENCE_MEAN = 1 };  /* p->reduction */
+enum { GRPO_HEAD_GRAD_F32 = 0, GRPO_HEAD_GRAD_BF16 = 1 };        /* p->grad_dtype */
+enum { GRPO_HEAD_TOKEN_MEAN = 0, GRPO_HEAD_SEQUENCE_MEAN = 1,
+       GRPO_HEAD_FIXED_CONSTANT = 2 };                          /* p->reduction */
 enum { GRPO_HEAD_LEVEL_TOKEN = 0, GRPO_HEAD_LEVEL_SEQUENCE_GSPO = 1 }; /* p->level */
 
 /* Parameter block, passed by host pointer.
@@ -105,9 +107,14 @@ enum { GRPO_HEAD_LEVEL_TOKEN = 0, GRPO_HEAD_LEVEL_SEQUENCE_GSPO = 1 }; /* p->lev
  *   dtype        GRPO_HEAD_BF16 or GRPO_HEAD_F32 (element type of H and W; the
  *                fp32 path keeps its dlogits in fp32, the bf16 path rounds them to
  *                bf16, nearest-even, before the two gradient products).
- *   reduction    token mean over active tokens, or mean over sequences (that have
- *                an active token) of each sequence's token mean.  GSPO always
- *                uses the sequence mean.
+ *   reduction    token mean over active tokens (global_active_tokens), mean over
+ *                sequences (that have an active token) of each sequence's token
+ *                mean (per_sequence_then_mean), or the sum over active tokens
+ *                divided by the caller's constant norm_const (fixed_constant, the
+ *                Dr. GRPO normaliser): RL-Kernel PR #291 "Add deterministic
+ *                DP-aware GRPO loss on the TP-aware logprob path", Key Changes
+ *                (LossReductionSpec.token_normalizer).  GSPO always uses the
+ *                sequence mean and rejects fixed_constant.
  *   level        token-level ratio (GRPO) or segment-level ratio (GSPO).
  *   validate     0: never synchronise.  1: synchronise `stream` once at the end of
  *                the call and check the conditions of statuses 3-5.
@@ -115,6 +122,21 @@ enum { GRPO_HEAD_LEVEL_TOKEN = 0, GRPO_HEAD_LEVEL_SEQUENCE_GSPO = 1 }; /* p->lev
  *   eps_low, eps_high  clip bounds >= 0 (eps_low < 1): ratio clipped to
  *                [1 - eps_low, 1 + eps_high].
  *   beta         KL weight >= 0.  beta > 0 needs ref_logp.
+ *   norm_const   fixed_constant only: the divisor C > 0 (finite); ignored otherwise.
+ *                The pages name the normaliser without fixing C (Dr. GRPO takes a
+ *                constant such as the generation budget times the group size).
+ *                With fixed_constant a batch without active tokens is not an
+ *                error even under validate (same page, review thread on the
+ *                zero-active-token guard): the loss is then 0.
+ *   accumulate_dw  0: grpo_head_bwd overwrites dW.  1: it adds this call's
+ *                gradient to dW (rows [0, v_real); the padding rows are left
+ *                as they are), e.g. across micro-batches.  dH is always
+ *                overwritten.
+ *   grad_dtype   element type of dH and dW: GRPO_HEAD_GRAD_F32 (0, the default)
+ *                or GRPO_HEAD_GRAD_BF16 (rounded to nearest even once, after the
+ *                fp32 accumulation; with several token chunks or accumulate_dw
+ *                the running dW is read back, added in fp32 and rounded again).
+ *   reserved     must be 0.
  */
 typedef struct grpo_head_params {
   int64_t n_tokens;
@@ -132,6 +154,10 @@ typedef struct grpo_head_params {
   float eps_low;
   float eps_high;
   float beta;
+  float norm_const;
+  int32_t accumulate_dw;
+  int32_t grad_dtype;
+  int32_t reserved;
 } grpo_head_params;
 
 /* Bytes of device workspace grpo_head_fwd needs (per-tile partials, target
@@ -154,10 +180,10 @@ size_t grpo_head_workspace_size(const grpo_head_params* p);
  * ref_logp may be NULL iff beta == 0 (kl is then 0).  old_logp and ref_logp are
  * read for active tokens only.  With level == GSPO the objective stage is the one
  * gspo_segment_reduce runs.
- * Status 0, 1, 2, 6; with validate also 3, 4, 5 (outputs are then still written,
- * but may be meaningless).  With validate == 0 an active target outside
- * [0, v_real) gives logp = NaN for that token, and an invalid sid is clamped into
- * [0, n_seqs); neither is reported. */
+ * Status 0, 1, 2, 6; with validate also 3 (not with fixed_constant), 4, 5
+ * (outputs are then still written, but may be meaningless).  With validate == 0
+ * an active target outside [0, v_real) gives logp = NaN for that token, and an
+ * invalid sid is clamped into [0, n_seqs); neither is reported. */
 int grpo_head_fwd(const grpo_head_params* p, const void* H, const void* W, const int64_t* y,
                   const uint8_t* mask, const int32_t* sid, const float* adv,
                   const float* old_logp, const float* ref_logp, float* logp, float* lse,
@@ -170,13 +196,15 @@ int grpo_head_fwd(const grpo_head_params* p, const void* H, const void* W, const
  *   G[t, v] = grad_output * coef[t] * (1[v == y_t] - exp(z[t, v] - lse[t])) * inv_tau
  *   and G[t, :] = 0 for inactive tokens.
  * grad_output is a DEVICE pointer to one fp32 scalar, or NULL for 1.0.
- * dH and dW are overwritten.  Token chunks are processed in ascending order and
- * dW accumulates them in that order.
+ * dH is overwritten.  dW is overwritten, or with p->accumulate_dw the gradient
+ * is added to it (rows [0, v_real) only; the padding rows are not touched).
+ * Token chunks are processed in ascending order and dW accumulates them in that
+ * order.  dH and dW hold fp32 or bf16 elements (p->grad_dtype).
  * Status 0, 1, 2, 6; with validate also 4 (active target out of range) and 5
  * (non-finite lse or coef). */
 int grpo_head_bwd(const grpo_head_params* p, const void* H, const void* W, const int64_t* y,
                   const uint8_t* mask, const float* lse, const float* coef,
-                  const float* grad_output, float* dH, float* dW, void* ws, size_t ws_bytes,
+                  const float* grad_output, void* dH, void* dW, void* ws, size_t ws_bytes,
                   void* stream);
 
 /* GSPO segment stage alone (no GEMM), from given per-token log-probs.

@@ -16,7 +16,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libgrpo_head.so")
 
 BF16, F32 = 0, 1
-TOKEN_MEAN, SEQUENCE_MEAN = 0, 1
+TOKEN_MEAN, SEQUENCE_MEAN, FIXED_CONSTANT = 0, 1, 2
+GRAD_F32, GRAD_BF16 = 0, 1
 LEVEL_TOKEN, LEVEL_SEQUENCE_GSPO = 0, 1
 
 STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "WORKSPACE_TOO_SMALL", 3: "NO_ACTIVE_TOKENS",
@@ -51,7 +52,9 @@ class Params(ctypes.Structure):
                 ("reduction", ctypes.c_int32), ("level", ctypes.c_int32),
                 ("validate", ctypes.c_int32), ("inv_tau", ctypes.c_float),
                 ("eps_low", ctypes.c_float), ("eps_high", ctypes.c_float),
-                ("beta", ctypes.c_float)]
+                ("beta", ctypes.c_float), ("norm_const", ctypes.c_float),
+                ("accumulate_dw", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 def _load():
@@ -86,17 +89,22 @@ lib = _load()
 def make_params(*, n_tokens, d_model, v_real, v_rows=None, n_seqs, dtype="bf16",
                 reduction="token_mean", level="token", inv_tau=1.0, eps_low=0.2,
                 eps_high=0.2, beta=0.0, ignore_index=-100, chunk_tokens=0,
-                validate=False) -> Params:
+                validate=False, norm_const=0.0, accumulate_dw=False,
+                grad_dtype="f32") -> Params:
     return Params(n_tokens=n_tokens, d_model=d_model, v_real=v_real,
                   v_rows=v_real if v_rows is None else v_rows, n_seqs=n_seqs,
                   ignore_index=ignore_index, chunk_tokens=chunk_tokens,
                   dtype={"bf16": BF16, "f32": F32}[dtype] if isinstance(dtype, str) else dtype,
-                  reduction={"token_mean": TOKEN_MEAN, "sequence_mean": SEQUENCE_MEAN}[reduction]
+                  reduction={"token_mean": TOKEN_MEAN, "sequence_mean": SEQUENCE_MEAN,
+                             "fixed_constant": FIXED_CONSTANT}[reduction]
                   if isinstance(reduction, str) else reduction,
                   level={"token": LEVEL_TOKEN, "sequence_gspo": LEVEL_SEQUENCE_GSPO}[level]
                   if isinstance(level, str) else level,
                   validate=int(bool(validate)), inv_tau=inv_tau, eps_low=eps_low,
-                  eps_high=eps_high, beta=beta)
+                  eps_high=eps_high, beta=beta, norm_const=norm_const,
+                  accumulate_dw=int(accumulate_dw),
+                  grad_dtype={"f32": GRAD_F32, "bf16": GRAD_BF16}[grad_dtype]
+                  if isinstance(grad_dtype, str) else grad_dtype, reserved=0)
 
 
 def _ptr(t):
@@ -205,10 +213,11 @@ class GrpoHead:
         return self.out3
 
     def bwd(self, H, W, y, mask, grad_output=None, dH=None, dW=None, stream=None):
+        gdt = torch.bfloat16 if self.p.grad_dtype == GRAD_BF16 else torch.float32
         if dH is None:
-            dH = torch.empty(self.p.n_tokens, self.p.d_model, dtype=torch.float32, device=H.device)
+            dH = torch.empty(self.p.n_tokens, self.p.d_model, dtype=gdt, device=W.device)
         if dW is None:
-            dW = torch.empty(self.p.v_rows, self.p.d_model, dtype=torch.float32, device=W.device)
+            dW = torch.empty(self.p.v_rows, self.p.d_model, dtype=gdt, device=W.device)
         grpo_head_bwd(self.p, H, W, y, mask, self.lse, self.coef, grad_output, dH, dW, self.ws,
                       stream=stream)
         return dH, dW

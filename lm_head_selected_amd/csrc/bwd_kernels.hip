@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
 struct ProductArgs {
   Operand A, B;
   int nk;                         // K stages
-  float* out; int64_t ld_out;     // elements between out rows
+  void* out; int64_t ld_out;      // elements (of O) between out rows
   int64_t m_limit;                // M extent written
   int64_t n_limit;                // N extent written
   int64_t zero_from;              // dW rows (N) >= this are written as 0 (padded vocab)
@@ -161,7 +161,28 @@ struct ProductArgs {
   int group_m;
 };
 
-template <typename T, int kRole>
+// Output element stores: fp32, or bf16 rounded to nearest even.
+__device__ __forceinline__ float load_out(const float* p) { return *p; }
+__device__ __forceinline__ float load_out(const __bf16* p) { return (float)*p; }
+__device__ __forceinline__ void store_out(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_out(__bf16* p, float v) {
+  const __bf16 b = (__bf16)v;
+  __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, b), (uint16_t*)p);
+}
+__device__ __forceinline__ f32x4 load_out4(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ f32x4 load_out4(const __bf16* p) {
+  const bf16x4 b = *(const bf16x4*)p;
+  return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
+__device__ __forceinline__ void store_out4(float* p, f32x4 v) {
+  __builtin_nontemporal_store(v, (f32x4*)p);
+}
+__device__ __forceinline__ void store_out4(__bf16* p, f32x4 v) {
+  const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+  __builtin_nontemporal_store(__builtin_bit_cast(i32x2, b), (i32x2*)p);
+}
+
+template <typename T, int kRole, typename O>
 __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int tiles_m,
                                                            int tiles_n) {
   __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
@@ -187,9 +208,9 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (m + e >= a.m_limit) continue;
-          float* p = a.out + (m + e) * a.ld_out + n;
-          const float v = a.accumulate ? acc[i][j][e] + *p : acc[i][j][e];
-          __builtin_nontemporal_store(v, p);
+          O* p = (O*)a.out + (m + e) * a.ld_out + n;
+          const float v = a.accumulate ? acc[i][j][e] + load_out(p) : acc[i][j][e];
+          store_out(p, v);
         }
       }
     }
@@ -219,10 +240,10 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
         const int64_t n = n0 + p * 128 + r, m = m0 + c * 4;
         if (n < a.n_limit && m < a.m_limit) {
           f32x4 v = *(const f32x4*)(L + r * 256 + ((c ^ (r & 15)) << 2));
-          float* o = a.out + n * a.ld_out + m;
+          O* o = (O*)a.out + n * a.ld_out + m;
           if (n >= a.zero_from) v = f32x4{0.f, 0.f, 0.f, 0.f};
-          else if (a.accumulate) v += *(const f32x4*)o;
-          __builtin_nontemporal_store(v, (f32x4*)o);
+          else if (a.accumulate) v += load_out4(o);
+          store_out4(o, v);
         }
       }
       __syncthreads();
@@ -267,7 +288,7 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, typename O>
 static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   const WsLayout& L = *a.L;
   const int64_t esz = sizeof(T);
@@ -276,13 +297,16 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   char* ht = a.ws + L.ht;
   float2* gl = (float2*)(a.ws + L.gl);
 
-  // padded vocabulary rows of dW that no tile reaches
-  if (a.v_rows > VK) {
-    hipError_t e = launch_fill_zero(a.dW + VK * D, (size_t)(a.v_rows - VK) * D * 4, s);
+  O* dW = (O*)a.dW;
+  O* dH = (O*)a.dH;
+  // padded vocabulary rows of dW that no tile reaches (left alone when accumulating)
+  if (a.v_rows > VK && !a.accumulate_dw) {
+    hipError_t e = launch_fill_zero(dW + VK * D, (size_t)(a.v_rows - VK) * D * sizeof(O), s);
     if (e != hipSuccess) return e;
   }
   if (N == 0) {
-    return launch_fill_zero(a.dW, (size_t)(a.v_rows < VK ? a.v_rows : VK) * D * 4, s);
+    if (a.accumulate_dw) return hipSuccess;
+    return launch_fill_zero(dW, (size_t)(a.v_rows < VK ? a.v_rows : VK) * D * sizeof(O), s);
   }
   const StageEvents& ev = *a.marks;
 
@@ -313,9 +337,9 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     // W rows >= v_real are never read (they load as zeros).
     ProductArgs ph{nt_vtiled(dz, R, esz, (int64_t)tiles_v * R * 256 * esz),
                    mn_row_major(a.W, D * esz, a.v_real, D, esz), (int)(VK * esz / kStageBytes),
-                   a.dH + c0 * D, D, nc, D, INT64_MAX, 0, a.group_dh};
-    hipLaunchKernelGGL((product_kernel<T, 0>), dim3(tiles_t * tiles_d), dim3(kThreads), 0, s, ph,
-                       tiles_t, tiles_d);
+                   dH + c0 * D, D, nc, D, INT64_MAX, 0, a.group_dh};
+    hipLaunchKernelGGL((product_kernel<T, 0, O>), dim3(tiles_t * tiles_d), dim3(kThreads), 0, s,
+                       ph, tiles_t, tiles_d);
     ev.mark(8, s);
 
     // HT of the chunk: D rows of ncp tokens (zero past nc)
@@ -325,12 +349,15 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
                        (const E*)Hc, D, nc, (E*)ht, R, ttd);
     ev.mark(9, s);
 
-    // dW: M = d (HT K-contiguous), N = v (dz read MN-contiguous), K = t
+    // dW: M = d (HT K-contiguous), N = v (dz read MN-contiguous), K = t.  Rows
+    // [v_real, VK) of the last tile are written as zeros, or, when accumulating
+    // into the caller's dW, not written at all.
     ProductArgs pw{nt_row_major(ht, R * esz, D), mn_vtiled(dz, R, esz, tiles_v),
-                   (int)(ncp * esz / kStageBytes), a.dW, D, D, (a.v_rows < VK ? a.v_rows : VK),
-                   a.v_real, c0 > 0 ? 1 : 0, a.group_dw};
-    hipLaunchKernelGGL((product_kernel<T, 1>), dim3(tiles_d * tiles_v), dim3(kThreads), 0, s, pw,
-                       tiles_d, tiles_v);
+                   (int)(ncp * esz / kStageBytes), dW, D, D,
+                   a.accumulate_dw ? a.v_real : (a.v_rows < VK ? a.v_rows : VK), a.v_real,
+                   (c0 > 0 || a.accumulate_dw) ? 1 : 0, a.group_dw};
+    hipLaunchKernelGGL((product_kernel<T, 1, O>), dim3(tiles_d * tiles_v), dim3(kThreads), 0, s,
+                       pw, tiles_d, tiles_v);
     ev.mark(10, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -339,7 +366,8 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd(int dtype, const BwdArgs& a, hipStream_t s) {
-  return dtype == 0 ? run_bwd<__bf16>(a, s) : run_bwd<float>(a, s);
+  if (a.grad_bf16) return dtype == 0 ? run_bwd<__bf16, __bf16>(a, s) : run_bwd<float, __bf16>(a, s);
+  return dtype == 0 ? run_bwd<__bf16, float>(a, s) : run_bwd<float, float>(a, s);
 }
 
 }  // namespace gh

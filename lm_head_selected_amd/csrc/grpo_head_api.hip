@@ -56,8 +56,20 @@ int check_common(const grpo_head_params* p, bool need_gemm) {
   if (p->n_seqs > (int64_t(1) << 31) - 1) return fail(GRPO_HEAD_INVALID_ARGUMENT, "n_seqs too large");
   if (p->level != GRPO_HEAD_LEVEL_TOKEN && p->level != GRPO_HEAD_LEVEL_SEQUENCE_GSPO)
     return fail(GRPO_HEAD_INVALID_ARGUMENT, "unknown level %d", p->level);
-  if (p->reduction != GRPO_HEAD_TOKEN_MEAN && p->reduction != GRPO_HEAD_SEQUENCE_MEAN)
+  if (p->reduction != GRPO_HEAD_TOKEN_MEAN && p->reduction != GRPO_HEAD_SEQUENCE_MEAN &&
+      p->reduction != GRPO_HEAD_FIXED_CONSTANT)
     return fail(GRPO_HEAD_INVALID_ARGUMENT, "unknown reduction %d", p->reduction);
+  if (p->reduction == GRPO_HEAD_FIXED_CONSTANT) {
+    if (p->level != GRPO_HEAD_LEVEL_TOKEN)
+      return fail(GRPO_HEAD_INVALID_ARGUMENT, "fixed_constant applies to the token level only");
+    if (!(p->norm_const > 0.0f) || !std::isfinite(p->norm_const))
+      return fail(GRPO_HEAD_INVALID_ARGUMENT, "norm_const must be finite and > 0");
+  }
+  if (p->accumulate_dw != 0 && p->accumulate_dw != 1)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "accumulate_dw must be 0 or 1");
+  if (p->grad_dtype != GRPO_HEAD_GRAD_F32 && p->grad_dtype != GRPO_HEAD_GRAD_BF16)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "unknown grad_dtype %d", p->grad_dtype);
+  if (p->reserved != 0) return fail(GRPO_HEAD_INVALID_ARGUMENT, "reserved must be 0");
   if (!(p->eps_low >= 0.0f && p->eps_low < 1.0f))
     return fail(GRPO_HEAD_INVALID_ARGUMENT, "eps_low must be in [0, 1)");
   if (!(p->eps_high >= 0.0f) || !std::isfinite(p->eps_high))
@@ -202,6 +214,7 @@ int run_loss(const grpo_head_params* p, const gh::WsLayout& L, char* ws, const f
   la.eps_low = p->eps_low;
   la.eps_high = p->eps_high;
   la.beta = p->beta;
+  la.norm_const = p->norm_const;
   la.logp = logp;
   la.old_logp = old_logp;
   la.ref_logp = ref_logp;
@@ -288,7 +301,8 @@ int grpo_head_fwd(const grpo_head_params* p, const void* H, const void* W, const
                         lse, logp, old_logp, ref_logp, out3, (uint32_t*)(w + L.flags)};
     e = gh::launch_validate(va, s);
     if (e != hipSuccess) return hip_fail(e, "validation kernel");
-    return finish_validation((uint32_t*)(w + L.flags), s, true);
+    return finish_validation((uint32_t*)(w + L.flags), s,
+                             p->reduction != GRPO_HEAD_FIXED_CONSTANT);
   }
   return ok();
 }
@@ -330,7 +344,7 @@ int grpo_head_logp(const grpo_head_params* p, const void* H, const void* W, cons
 
 int grpo_head_bwd(const grpo_head_params* p, const void* H, const void* W, const int64_t* y,
                   const uint8_t* mask, const float* lse, const float* coef,
-                  const float* grad_output, float* dH, float* dW, void* ws, size_t ws_bytes,
+                  const float* grad_output, void* dH, void* dW, void* ws, size_t ws_bytes,
                   void* stream) {
   int rc = check_common(p, true);
   if (rc) return rc;
@@ -350,7 +364,8 @@ int grpo_head_bwd(const grpo_head_params* p, const void* H, const void* W, const
                  p->v_real, p->v_rows, p->ignore_index, p->inv_tau, w, &L,
                  logit_group(L.chunk < p->n_tokens ? L.chunk : p->n_tokens, p->d_model,
                              p->dtype == GRPO_HEAD_F32 ? 4 : 2),
-                 kGroupDh, kGroupDw, &g_marks};
+                 kGroupDh, kGroupDw, &g_marks, p->accumulate_dw,
+                 p->grad_dtype == GRPO_HEAD_GRAD_BF16 ? 1 : 0};
   hipError_t e = gh::launch_bwd(p->dtype, ba, s);
   if (e != hipSuccess) return hip_fail(e, "backward kernels");
   if (p->validate) {

@@ -56,6 +56,7 @@ struct MergeArgs {
 struct LossArgs {
   int64_t n_tokens; int64_t n_seqs; int32_t level, reduction;
   float eps_low, eps_high, beta;
+  float norm_const;  // fixed_constant divisor (reduction 2)
   const float* logp; const float* old_logp; const float* ref_logp; const float* adv;
   const int32_t* sid; const uint8_t* mask; const int64_t* y; int64_t ignore_index;
   int32_t* seq_L; float* seq_F; float* seq_G; float* scal;
@@ -81,12 +82,14 @@ struct StageEvents {
 struct BwdArgs {
   const void* H; const void* W; const int64_t* y; const uint8_t* mask;
   const float* lse; const float* coef; const float* grad_output;
-  float* dH; float* dW;
+  void* dH; void* dW;
   int64_t n_tokens, d_model, v_real, v_rows, ignore_index;
   float inv_tau;
   char* ws; const WsLayout* L;
   int group_fwd, group_dh, group_dw;
   const StageEvents* marks;
+  int accumulate_dw;   // add the gradient to dW rows [0, v_real) instead of overwriting
+  int grad_bf16;       // dH and dW are bf16 (else fp32)
 };
 
 // records stage event 1 after the tile launch

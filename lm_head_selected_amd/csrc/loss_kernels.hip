@@ -5,11 +5,13 @@
 // depend on the layout, so those sums are pinned to one order: tokens of a
 // sequence in a fixed strided-then-tree order, then sequences in a fixed tree
 // order (RL-Kernel PR #291, Overview / Key Changes).  Normalisers:
-// token mean over active tokens (global_active_tokens) or mean over sequences
+// token mean over active tokens (global_active_tokens), mean over sequences
 // with at least one active token of each sequence's token mean
-// (per_sequence_then_mean).  GSPO aggregates m_t (logp_t - old_t) per segment
-// (the index_add of Fast-LLM PR #554, What), then forms the segment ratio, the
-// loss, the new_logprobs metric and the unscaled per-token coefficient.
+// (per_sequence_then_mean), or the active-token sum over a caller constant
+// (fixed_constant, the Dr. GRPO normaliser; same page, Key Changes).  GSPO
+// aggregates m_t (logp_t - old_t) per segment (the index_add of Fast-LLM PR #554,
+// What), then forms the segment ratio, the loss, the new_logprobs metric and the
+// unscaled per-token coefficient.
 // An empty batch yields zeros, never a division by zero.
 #include <hip/hip_runtime.h>
 
@@ -96,7 +98,8 @@ __global__ __launch_bounds__(kSeqThreads) void seq_totals_kernel(LossArgs a) {
 }
 
 // Scalars.  One workgroup of 1024 threads over all sequences.
-// scal[0] = 1/T_act, scal[1] = 1/S_live (0 for an empty batch).
+// scal[0] = 1/T_act (1/norm_const for fixed_constant), scal[1] = 1/S_live (0 for an
+// empty batch).
 __global__ __launch_bounds__(kRedThreads) void loss_scalars_kernel(LossArgs a) {
   __shared__ float sh[6][kRedThreads];
   const float clo = 1.0f - a.eps_low, chi = 1.0f + a.eps_high;
@@ -135,7 +138,11 @@ __global__ __launch_bounds__(kRedThreads) void loss_scalars_kernel(LossArgs a) {
   if (threadIdx.x == 0) {
     const float T = v[0], S = v[1];
     float pol = 0.f, kl = 0.f;
-    if (T > 0.f) {
+    const bool fixed = a.level == 0 && a.reduction == 2;
+    if (fixed) {
+      pol = v[2] / a.norm_const;
+      kl = v[3] / a.norm_const;
+    } else if (T > 0.f) {
       if (a.level == 0 && a.reduction == 0) {
         pol = v[2] / T;
         kl = v[3] / T;
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(kRedThreads) void loss_scalars_kernel(LossArgs a) {
     a.out3[0] = pol + a.beta * kl;
     a.out3[1] = pol;
     a.out3[2] = kl;
-    a.scal[0] = T > 0.f ? 1.0f / T : 0.f;
+    a.scal[0] = fixed ? 1.0f / a.norm_const : (T > 0.f ? 1.0f / T : 0.f);
     a.scal[1] = S > 0.f ? 1.0f / S : 0.f;
   }
 }
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(256) void coef_kernel(LossArgs a) {
     const float wseq = L > 0.f ? invS / L : 0.f;
     const float dkl = a.ref_logp ? 1.0f - expf(a.ref_logp[t] - lp) : 0.0f;
     if (a.level == 0) {
-      const float w = a.reduction == 0 ? invT : wseq;
+      const float w = a.reduction == 1 ? wseq : invT;   // token mean or fixed constant
       const float adv = a.adv[s];
       const float r = expf(lp - a.old_logp[t]);
       const float c = fminf(fmaxf(r, 1.0f - a.eps_low), 1.0f + a.eps_high);

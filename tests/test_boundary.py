@@ -30,8 +30,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_params_struct_layout_matches_header():
-    # 7 int64 + 4 int32 + 4 float, no padding
-    assert ctypes.sizeof(gb.Params) == 7 * 8 + 4 * 4 + 4 * 4
+    # 7 int64 + 4 int32 + 5 float + 3 int32, no padding
+    assert ctypes.sizeof(gb.Params) == 7 * 8 + 4 * 4 + 5 * 4 + 3 * 4
     text = open(HEADER).read()
     body = re.search(r"typedef struct grpo_head_params \{(.*?)\}", text, re.S).group(1)
     fields = re.findall(r"\b(\w+);", body)
@@ -46,6 +46,11 @@ def P(**kw):
 
 
 def test_workspace_sizes():
+    assert gb.fwd_workspace_size(P(reduction="fixed_constant", norm_const=4096.0)) > 0
+    assert gb.workspace_size(P(grad_dtype="bf16", accumulate_dw=True)) > 0
+    bad = P()
+    bad.reserved = 1
+    assert gb.workspace_size(bad) == 0
     p = P()
     fwd = gb.fwd_workspace_size(p)
     full = gb.workspace_size(p)
@@ -66,7 +71,11 @@ def test_workspace_sizes():
                                  dict(dtype=7), dict(reduction=5), dict(level=3),
                                  dict(inv_tau=0.0), dict(eps_low=1.0), dict(eps_low=-0.1),
                                  dict(beta=-1.0), dict(inv_tau=float("nan")),
-                                 dict(chunk_tokens=-5)])
+                                 dict(chunk_tokens=-5), dict(reduction="fixed_constant"),
+                                 dict(reduction="fixed_constant", norm_const=-2.0),
+                                 dict(reduction="fixed_constant", norm_const=8.0,
+                                      level="sequence_gspo"),
+                                 dict(grad_dtype=5), dict(accumulate_dw=3)])
 def test_invalid_params_rejected_without_gpu(bad):
     p = P(**bad)
     assert gb.workspace_size(p) == 0
