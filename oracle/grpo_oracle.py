@@ -51,7 +51,7 @@ import numpy as np
 __all__ = [
     "widen", "active_tokens", "logits_rows", "lse_rows", "forward", "tile_partials",
     "tiled_lse", "sequence_counts", "grpo_objective", "gspo_objective", "objective",
-    "dlogits_rows", "backward", "dH_rows", "dW_rows",
+    "dlogits_rows", "backward", "dH_rows", "dW_rows", "group_advantage",
 ]
 
 
@@ -291,6 +291,41 @@ def objective(inp: dict, logp) -> dict:
     return grpo_objective(logp, inp["old_logp"], inp["ref_logp"], inp["adv"], inp["sid"], active,
                           inp["n_seqs"], inp["eps_low"], inp["eps_high"], inp["beta"],
                           inp["reduction"], inp.get("norm_const"))
+
+
+# ---------------------------------------------------------------------------
+# advantage (the step before the path)
+# ---------------------------------------------------------------------------
+def group_advantage(rewards, group_size: int, eps: float, scale_by_std: bool = True):
+    """Group-relative advantage of each sequence from its scalar reward.
+
+    Sequences come in consecutive groups of ``group_size`` (the completions of one
+    prompt).  Per group g with rewards r_i:
+      mean_g = sum_i r_i / G,
+      var_g  = sum_i (r_i - mean_g)^2 / G      (two passes: the mean is subtracted
+                                                before squaring),
+      A_i    = (r_i - mean_g) / (sqrt(var_g) + eps)   or, without the std
+               scaling (the Dr. GRPO choice), A_i = r_i - mean_g.
+    Sources: the group-relative advantage acts per sequence (RL-Kernel PR #291,
+    Overview); the two-pass variance subtracts the mean before squaring (same
+    page, review thread on the TWO_PASS enum).  The pages fix neither the divisor
+    of the variance nor eps; reading: the population variance of the group
+    (divide by G) and a caller eps >= 0.
+    """
+    r = np.asarray(rewards, np.float64)
+    if group_size < 1 or len(r) % group_size:
+        raise ValueError("the number of sequences must be a multiple of group_size")
+    out = np.zeros(len(r))
+    for g0 in range(0, len(r), group_size):
+        grp = r[g0:g0 + group_size]
+        mean = sum(grp) / group_size
+        dev = grp - mean
+        if scale_by_std:
+            var = sum(dev * dev) / group_size
+            out[g0:g0 + group_size] = dev / (np.sqrt(var) + eps)
+        else:
+            out[g0:g0 + group_size] = dev
+    return out
 
 
 # ---------------------------------------------------------------------------
