@@ -304,8 +304,9 @@ def group_advantage(rewards, group_size: int, eps: float, scale_by_std: bool = T
       mean_g = sum_i r_i / G,
       var_g  = sum_i (r_i - mean_g)^2 / G      (two passes: the mean is subtracted
                                                 before squaring),
-      A_i    = (r_i - mean_g) / (sqrt(var_g) + eps)   or, without the std
-               scaling (the Dr. GRPO choice), A_i = r_i - mean_g.
+      A_i    = (r_i - mean_g) / (sqrt(var_g) + eps)   (0 when that divisor is 0,
+               a constant group with eps = 0) or, without the std scaling (the
+               Dr. GRPO choice), A_i = r_i - mean_g.
     Sources: the group-relative advantage acts per sequence (RL-Kernel PR #291,
     Overview); the two-pass variance subtracts the mean before squaring (same
     page, review thread on the TWO_PASS enum).  The pages fix neither the divisor
@@ -322,7 +323,9 @@ def group_advantage(rewards, group_size: int, eps: float, scale_by_std: bool = T
         dev = grp - mean
         if scale_by_std:
             var = sum(dev * dev) / group_size
-            out[g0:g0 + group_size] = dev / (np.sqrt(var) + eps)
+            den = np.sqrt(var) + eps
+            # a constant group with eps = 0 has nothing to scale: its advantages are 0
+            out[g0:g0 + group_size] = dev / den if den > 0 else 0.0
         else:
             out[g0:g0 + group_size] = dev
     return out

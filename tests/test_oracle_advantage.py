@@ -55,6 +55,7 @@ def test_two_pass_survives_a_large_offset():
 def test_constant_group_and_singletons_give_zero():
     A = oracle.group_advantage([1.0, 1.0, 1.0, 0.0, 3.0, 7.0], 3, 1e-6)
     assert np.all(A[:3] == 0.0)
+    assert np.all(oracle.group_advantage([2.0, 2.0], 2, 0.0) == 0.0)   # 0/0 taken as 0
     assert np.all(oracle.group_advantage([0.3, -2.0, 5.0], 1, 1e-6) == 0.0)
 
 
