@@ -257,6 +257,26 @@ int grpo_head_logp(const grpo_head_params* p, const void* H, const void* W, cons
  * logits).  0 if p is invalid. */
 size_t grpo_head_logp_workspace_size(const grpo_head_params* p);
 
+/* Group-relative advantage of each sequence from its scalar reward: the step
+ * before the objective, whose adv input it fills.  Sequences come in consecutive
+ * groups of group_size (the completions of one prompt).  Per group:
+ *   mean = sum_i r_i / G, var = sum_i (r_i - mean)^2 / G (two passes: the mean is
+ *   subtracted before squaring), and
+ *   adv_i = (r_i - mean) / (sqrt(var) + eps)   (0 when that divisor is 0), or
+ *   adv_i = r_i - mean                         with scale_by_std = 0.
+ * Sources: RL-Kernel PR #291 "Add deterministic DP-aware GRPO loss on the
+ * TP-aware logprob path", Overview (the group-relative advantage acts per
+ * sequence) and the review thread on the TWO_PASS variance enum.  The pages fix
+ * neither the variance divisor nor eps: the population variance and a caller
+ * eps are used.  Each group's sums run in index order, so results are bitwise
+ * repeatable.
+ *   rewards, adv  [n_seqs] fp32 device buffers (adv may alias rewards);
+ *   group_size    G >= 1, dividing n_seqs; n_seqs >= 0 (0: nothing is enqueued);
+ *   eps           finite, >= 0;  scale_by_std  0 or 1.
+ * Status 0, 1, 6.  No workspace. */
+int grpo_group_advantage(const float* rewards, int64_t n_seqs, int64_t group_size, float eps,
+                         int32_t scale_by_std, float* adv, void* stream);
+
 /* Stage timing for measurement tools; off by default, process-wide, not for
  * concurrent use from several threads.  `events` holds `n_events` caller-created
  * hipEvent_t handles (cast to void*; NULL entries are skipped), or events == NULL

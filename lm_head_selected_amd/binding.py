@@ -26,7 +26,7 @@ STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "WORKSPACE_TOO_SMALL", 3: "NO_ACTIV
 EXPORTS = ("grpo_head_fwd_workspace_size", "grpo_head_workspace_size",
            "gspo_segment_workspace_size", "grpo_head_fwd", "grpo_head_bwd",
            "gspo_segment_reduce", "grpo_head_logp", "grpo_head_logp_workspace_size",
-           "grpo_head_set_stage_events", "grpo_head_last_error")
+           "grpo_group_advantage", "grpo_head_set_stage_events", "grpo_head_last_error")
 
 # stage-event slots recorded by grpo_head_fwd / grpo_head_bwd
 N_STAGE_EVENTS = 11
@@ -76,6 +76,9 @@ def _load():
     lib.gspo_segment_reduce.restype = i32
     lib.grpo_head_logp.argtypes = [pp] + [vp] * 6 + [vp, sz, vp]
     lib.grpo_head_logp.restype = i32
+    lib.grpo_group_advantage.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                         ctypes.c_int32, vp, vp]
+    lib.grpo_group_advantage.restype = i32
     lib.grpo_head_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     lib.grpo_head_set_stage_events.restype = i32
     lib.grpo_head_last_error.argtypes = []
@@ -183,6 +186,13 @@ def grpo_head_logp(p, H, W, y, mask, logp, lse, ws, ws_bytes=None, stream=None):
     ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check(lib.grpo_head_logp(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(y), _ptr(mask), _ptr(logp),
                               _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def grpo_group_advantage(rewards, group_size, eps, adv, scale_by_std=True, n_seqs=None,
+                         stream=None):
+    n = rewards.numel() if n_seqs is None else n_seqs
+    _check(lib.grpo_group_advantage(_ptr(rewards), n, group_size, eps, int(scale_by_std),
+                                    _ptr(adv), _stream(stream)))
 
 
 class GrpoHead:

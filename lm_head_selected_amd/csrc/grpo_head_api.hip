@@ -257,6 +257,25 @@ size_t gspo_segment_workspace_size(const grpo_head_params* p) {
 
 const char* grpo_head_last_error(void) { return g_last_error.c_str(); }
 
+int grpo_group_advantage(const float* rewards, int64_t n_seqs, int64_t group_size, float eps,
+                         int32_t scale_by_std, float* adv, void* stream) {
+  if (n_seqs < 0) return fail(GRPO_HEAD_INVALID_ARGUMENT, "n_seqs < 0");
+  if (group_size < 1) return fail(GRPO_HEAD_INVALID_ARGUMENT, "group_size must be >= 1");
+  if (n_seqs % group_size != 0)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "group_size %lld does not divide n_seqs %lld",
+                (long long)group_size, (long long)n_seqs);
+  if (!(eps >= 0.0f) || !std::isfinite(eps))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (scale_by_std != 0 && scale_by_std != 1)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "scale_by_std must be 0 or 1");
+  if (n_seqs > 0 && (!rewards || !adv))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "rewards and adv must not be NULL");
+  hipError_t e = gh::launch_group_advantage(rewards, n_seqs, group_size, eps, scale_by_std, adv,
+                                            (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "advantage kernel");
+  return ok();
+}
+
 int grpo_head_set_stage_events(void* const* events, int n_events) {
   if (n_events < 0 || n_events > 16)
     return fail(GRPO_HEAD_INVALID_ARGUMENT, "n_events must be in [0, 16]");

@@ -99,6 +99,8 @@ hipError_t launch_target_logit(int dtype, const TargetArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_loss(const LossArgs& a, hipStream_t s);
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
+hipError_t launch_group_advantage(const float* r, int64_t n_seqs, int64_t G, float eps,
+                                  int scale, float* adv, hipStream_t s);
 hipError_t launch_bwd(int dtype, const BwdArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 

@@ -202,6 +202,45 @@ hipError_t launch_loss(const LossArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Group-relative advantage of each sequence from its scalar reward: consecutive
+// groups of G sequences; mean, then the variance of the deviations (two passes,
+// the mean subtracted before squaring: RL-Kernel PR #291, review thread on the
+// TWO_PASS enum), divided by G; A = (r - mean) / (std + eps), 0 when that divisor
+// is 0, or A = r - mean without the std scaling.  One thread per group, each sum
+// in index order, so the result is bitwise repeatable.
+__global__ __launch_bounds__(256) void group_advantage_kernel(const float* __restrict__ r,
+                                                              int64_t n_groups, int64_t G,
+                                                              float eps, int scale,
+                                                              float* __restrict__ adv) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= n_groups) return;
+  const float* rg = r + g * G;
+  float* ag = adv + g * G;
+  float sum = 0.0f;
+  for (int64_t i = 0; i < G; ++i) sum += rg[i];
+  const float mean = sum / (float)G;
+  if (!scale) {
+    for (int64_t i = 0; i < G; ++i) ag[i] = rg[i] - mean;
+    return;
+  }
+  float ss = 0.0f;
+  for (int64_t i = 0; i < G; ++i) {
+    const float d = rg[i] - mean;
+    ss += d * d;
+  }
+  const float den = sqrtf(ss / (float)G) + eps;
+  for (int64_t i = 0; i < G; ++i) ag[i] = den > 0.0f ? (rg[i] - mean) / den : 0.0f;
+}
+
+hipError_t launch_group_advantage(const float* r, int64_t n_seqs, int64_t G, float eps,
+                                  int scale, float* adv, hipStream_t s) {
+  const int64_t n_groups = n_seqs / G;
+  if (n_groups == 0) return hipSuccess;
+  hipLaunchKernelGGL(group_advantage_kernel, dim3((unsigned)ceil_div(n_groups, 256)), dim3(256),
+                     0, s, r, n_groups, G, eps, scale, adv);
+  return hipGetLastError();
+}
+
 // Validation (only with validate = 1): one workgroup scans every token.
 __global__ __launch_bounds__(1024) void validate_kernel(ValidateArgs a) {
   __shared__ uint32_t sflag[1024];

@@ -155,3 +155,16 @@ def test_logp_entry_rejects_null_buffers_and_small_workspace():
         gb.grpo_head_logp(p, 1, 1, 1, None, 1, 1, 1, ws_bytes=gb.logp_workspace_size(p) - 1,
                           stream=0)
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("n,G,eps,scale", [(8, 0, 0.0, 1), (8, 3, 0.0, 1), (8, 4, -1.0, 1),
+                                           (8, 4, float("nan"), 1), (8, 4, 0.0, 2),
+                                           (-4, 4, 0.0, 1)])
+def test_advantage_rejects_bad_arguments(n, G, eps, scale):
+    rc = gb.lib.grpo_group_advantage(1, n, G, eps, scale, 1, 0)
+    assert rc == 1 and gb.lib.grpo_head_last_error().decode()
+
+
+def test_advantage_null_buffers_and_empty():
+    assert gb.lib.grpo_group_advantage(None, 8, 4, 0.0, 1, 1, 0) == 1
+    assert gb.lib.grpo_group_advantage(None, 0, 4, 0.0, 1, None, 0) == 0   # nothing to do
