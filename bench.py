@@ -250,6 +250,27 @@ def main():
     torch.cuda.synchronize()
     ms_logp = l0.elapsed_time(l1) / K2
 
+    # one GPU's share of a 2-way vocabulary-parallel forward: the tile stage on
+    # the first half of the vocabulary tiles (on the global tile grid), timed alone
+    n_vt = -(-V // 256)
+    v_half = (n_vt // 2) * 256
+    sh_part = torch.empty(gb.shard_partials_bytes(p, 0, v_half), dtype=torch.uint8, device=dev)
+    sh_zy = torch.empty(N, dtype=torch.float32, device=dev)
+    w_half = d["W"][:v_half]
+
+    def shard_call():
+        gb.grpo_head_shard_partials(p, 0, v_half, d["H"], w_half, d["y"], d["mask"], sh_part,
+                                    sh_zy, stream=stream)
+
+    shard_call()
+    torch.cuda.synchronize()
+    l0.record(stream)
+    for _ in range(K2):
+        shard_call()
+    l1.record(stream)
+    torch.cuda.synchronize()
+    ms_shard = l0.elapsed_time(l1) / K2
+
     stages = {}
     for name, (a, b) in gb.STAGES.items():
         stages[name] = float(np.mean([hev.elapsed_ms(evs[k][a], evs[k][b]) for k in range(K)]))
@@ -291,6 +312,8 @@ def main():
         "logp_entry": {"ms": round(ms_logp, 3), "calls": K2,
                        "tokens_per_s": round(N / (ms_logp / 1e3), 1),
                        "tflops_2nvd": round(2.0 * N * V * D / (ms_logp / 1e3) / 1e12, 1)},
+        "tp2_shard_tiles": {"v_rows": v_half, "ms": round(ms_shard, 3),
+                            "tflops": round(2.0 * N * v_half * D / (ms_shard / 1e3) / 1e12, 1)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)

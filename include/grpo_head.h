@@ -257,6 +257,48 @@ int grpo_head_logp(const grpo_head_params* p, const void* H, const void* W, cons
  * logits).  0 if p is invalid. */
 size_t grpo_head_logp_workspace_size(const grpo_head_params* p);
 
+/* One GPU's share of a vocabulary-parallel forward, part 1: the per-tile
+ * partials and the target logits of one vocabulary shard, on the global tile
+ * grid, so that a fixed-order merge of all shards' partials (part 2) is bitwise
+ * the single-GPU result whatever the number of shards.  RL-Kernel PR #291 "Add
+ * deterministic DP-aware GRPO loss on the TP-aware logprob path", commit notes
+ * (ShardingSpec; the tile size must divide every shard boundary for cross-degree
+ * bitwise equality; the fixed merge order) and the review thread on
+ * _local_tile_stats.
+ *   The shard is global vocabulary rows [v_begin, v_end), 0 <= v_begin < v_end <=
+ *   v_rows; v_begin must be a multiple of 256 (the vocabulary tile) and v_end
+ *   either a multiple of 256 or >= v_real.  W_shard points to the shard's first
+ *   row (v_end - v_begin rows of d_model elements); rows >= v_real are padding
+ *   and never read.  The shard's real rows [v_begin, min(v_end, v_real)) form
+ *   n_st = ceil((min(v_end, v_real) - v_begin) / 256) tiles, the global tiles
+ *   v_begin/256 .. + n_st - 1 (n_st may be 0 for a shard of padding only).
+ *   partials  [n_st][n_tokens] pairs of fp32 (base-2 max, sum of 2^(z log2 e -
+ *             max)) = grpo_head_shard_partials_bytes() bytes; the shards' arrays
+ *             concatenated in ascending shard order are the global
+ *             [ceil(v_real/256)][n_tokens] array part 2 reads.
+ *   zy        [n_tokens] fp32, written for every token: z[t, y_t] when y_t lies
+ *             in the shard's real rows and token t is active, else +0.0.  Adding
+ *             the shards' zy (in any order) gives every target logit exactly.
+ * Uses p->n_tokens, d_model, v_real, v_rows, ignore_index, dtype, inv_tau.
+ * Status 0, 1, 6.  No workspace. */
+int grpo_head_shard_partials(const grpo_head_params* p, int64_t v_begin, int64_t v_end,
+                             const void* H, const void* W_shard, const int64_t* y,
+                             const uint8_t* mask, void* partials, float* zy, void* stream);
+
+/* Bytes of grpo_head_shard_partials' partials output for that shard; 0 if the
+ * parameters or the shard bounds are invalid. */
+size_t grpo_head_shard_partials_bytes(const grpo_head_params* p, int64_t v_begin,
+                                      int64_t v_end);
+
+/* Part 2: the fixed-order merge of all shards' partials (concatenated in global
+ * tile order) into logp and lse, exactly as grpo_head_logp forms them:
+ *   logp[t] = zy[t] - lse[t] for active tokens, 0 for inactive ones.
+ * Bitwise equal to grpo_head_logp's outputs when the shards tile the vocabulary
+ * as part 1 requires.  Uses the same fields as grpo_head_logp.  Status 0, 1, 6. */
+int grpo_head_merge_partials(const grpo_head_params* p, const void* partials, const float* zy,
+                             const int64_t* y, const uint8_t* mask, float* logp, float* lse,
+                             void* stream);
+
 /* Group-relative advantage of each sequence from its scalar reward: the step
  * before the objective, whose adv input it fills.  Sequences come in consecutive
  * groups of group_size (the completions of one prompt).  Per group:

@@ -26,7 +26,8 @@ STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "WORKSPACE_TOO_SMALL", 3: "NO_ACTIV
 EXPORTS = ("grpo_head_fwd_workspace_size", "grpo_head_workspace_size",
            "gspo_segment_workspace_size", "grpo_head_fwd", "grpo_head_bwd",
            "gspo_segment_reduce", "grpo_head_logp", "grpo_head_logp_workspace_size",
-           "grpo_group_advantage", "grpo_head_set_stage_events", "grpo_head_last_error")
+           "grpo_group_advantage", "grpo_head_shard_partials", "grpo_head_shard_partials_bytes",
+           "grpo_head_merge_partials", "grpo_head_set_stage_events", "grpo_head_last_error")
 
 # stage-event slots recorded by grpo_head_fwd / grpo_head_bwd
 N_STAGE_EVENTS = 11
@@ -79,6 +80,13 @@ def _load():
     lib.grpo_group_advantage.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                          ctypes.c_int32, vp, vp]
     lib.grpo_group_advantage.restype = i32
+    i64 = ctypes.c_int64
+    lib.grpo_head_shard_partials.argtypes = [pp, i64, i64] + [vp] * 6 + [vp]
+    lib.grpo_head_shard_partials.restype = i32
+    lib.grpo_head_shard_partials_bytes.argtypes = [pp, i64, i64]
+    lib.grpo_head_shard_partials_bytes.restype = sz
+    lib.grpo_head_merge_partials.argtypes = [pp] + [vp] * 6 + [vp]
+    lib.grpo_head_merge_partials.restype = i32
     lib.grpo_head_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     lib.grpo_head_set_stage_events.restype = i32
     lib.grpo_head_last_error.argtypes = []
@@ -193,6 +201,22 @@ def grpo_group_advantage(rewards, group_size, eps, adv, scale_by_std=True, n_seq
     n = rewards.numel() if n_seqs is None else n_seqs
     _check(lib.grpo_group_advantage(_ptr(rewards), n, group_size, eps, int(scale_by_std),
                                     _ptr(adv), _stream(stream)))
+
+
+def shard_partials_bytes(p, v_begin, v_end) -> int:
+    return lib.grpo_head_shard_partials_bytes(ctypes.byref(p), v_begin, v_end)
+
+
+def grpo_head_shard_partials(p, v_begin, v_end, H, W_shard, y, mask, partials, zy,
+                             stream=None):
+    _check(lib.grpo_head_shard_partials(ctypes.byref(p), v_begin, v_end, _ptr(H), _ptr(W_shard),
+                                        _ptr(y), _ptr(mask), _ptr(partials), _ptr(zy),
+                                        _stream(stream)))
+
+
+def grpo_head_merge_partials(p, partials, zy, y, mask, logp, lse, stream=None):
+    _check(lib.grpo_head_merge_partials(ctypes.byref(p), _ptr(partials), _ptr(zy), _ptr(y),
+                                        _ptr(mask), _ptr(logp), _ptr(lse), _stream(stream)))
 
 
 class GrpoHead:

@@ -114,12 +114,16 @@ __global__ __launch_bounds__(256) void target_logit_kernel(TargetArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.n_tokens) return;
-  if (!token_active(a.mask, a.y, a.ignore_index, t)) return;
-  const int64_t yy = a.y[t];
-  if (yy < 0 || yy >= a.v_real) return;
+  const bool act = token_active(a.mask, a.y, a.ignore_index, t);
+  const int64_t yy = act ? a.y[t] : -1;
+  const int64_t yl = yy - a.v_begin;                 // row within this W
+  if (!act || yl < 0 || yl >= a.v_real) {
+    if (a.mode == 2 && lane == 0) a.zy[t] = 0.0f;    // not this shard's target
+    return;
+  }
   constexpr int kPer = 16 / (int)sizeof(T);          // elements per 16-byte chunk
   const T* h = (const T*)a.H + t * a.d_model;
-  const T* w = (const T*)a.W + yy * a.d_model;
+  const T* w = (const T*)a.W + yl * a.d_model;
   float acc = 0.0f;
   for (int64_t d0 = (int64_t)lane * kPer; d0 < a.d_model; d0 += 64 * kPer) {
     const i32x4 hv = *(const i32x4*)(h + d0);
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(256) void target_logit_kernel(TargetArgs a) {
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
   if (lane != 0) return;
   const float z = acc * a.inv_tau;
-  if (a.mode == 0) {
+  if (a.mode != 1) {
     a.zy[t] = z;
   } else {
     const float g = a.grad_output ? *a.grad_output * a.coef[t] * a.inv_tau

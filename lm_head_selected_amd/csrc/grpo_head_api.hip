@@ -236,6 +236,23 @@ int run_loss(const grpo_head_params* p, const gh::WsLayout& L, char* ws, const f
   return GRPO_HEAD_OK;
 }
 
+// Shard bounds of grpo_head_shard_partials; returns the shard's real row count.
+int check_shard(const grpo_head_params* p, int64_t v_begin, int64_t v_end, int64_t* real_rows) {
+  if (!p) return fail(GRPO_HEAD_INVALID_ARGUMENT, "params is NULL");
+  int rc = check_gemm(p);
+  if (rc) return rc;
+  if (v_begin < 0 || v_end <= v_begin || v_end > p->v_rows)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "shard [%lld, %lld) outside [0, v_rows)",
+                (long long)v_begin, (long long)v_end);
+  if (v_begin % gh::kVocabTile != 0 || (v_end % gh::kVocabTile != 0 && v_end < p->v_real))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT,
+                "shard bounds must lie on the %d-row tile grid (or the end at or past v_real)",
+                gh::kVocabTile);
+  const int64_t hi = v_end < p->v_real ? v_end : p->v_real;
+  *real_rows = hi > v_begin ? hi - v_begin : 0;
+  return GRPO_HEAD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,6 +273,54 @@ size_t gspo_segment_workspace_size(const grpo_head_params* p) {
 }
 
 const char* grpo_head_last_error(void) { return g_last_error.c_str(); }
+
+size_t grpo_head_shard_partials_bytes(const grpo_head_params* p, int64_t v_begin,
+                                      int64_t v_end) {
+  int64_t rows = 0;
+  if (check_shard(p, v_begin, v_end, &rows) != GRPO_HEAD_OK) return 0;
+  return (size_t)gh::ceil_div(rows, gh::kVocabTile) * (size_t)p->n_tokens * 8;
+}
+
+int grpo_head_shard_partials(const grpo_head_params* p, int64_t v_begin, int64_t v_end,
+                             const void* H, const void* W_shard, const int64_t* y,
+                             const uint8_t* mask, void* partials, float* zy, void* stream) {
+  int64_t rows = 0;
+  int rc = check_shard(p, v_begin, v_end, &rows);
+  if (rc) return rc;
+  if (p->n_tokens == 0) return ok();
+  if (!H || !W_shard || !y || !zy || (rows > 0 && !partials))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "a required buffer is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t n_st = gh::ceil_div(rows, gh::kVocabTile);
+  if (n_st > 0) {
+    gh::FwdTileArgs fa{W_shard, H, p->n_tokens, p->d_model, rows, p->inv_tau, (float2*)partials,
+                       logit_group(p->n_tokens, p->d_model, p->dtype == GRPO_HEAD_F32 ? 4 : 2)};
+    hipError_t e = gh::launch_fwd_tiles(p->dtype, fa, n_st, gh::StageEvents{}, s);
+    if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
+  }
+  gh::TargetArgs ta{H, W_shard, y, mask, p->n_tokens, p->d_model, rows, p->ignore_index,
+                    p->inv_tau, 2, zy, nullptr, nullptr, nullptr, nullptr, 0, v_begin};
+  hipError_t e = gh::launch_target_logit(p->dtype, ta, s);
+  if (e != hipSuccess) return hip_fail(e, "target logit kernel");
+  return ok();
+}
+
+int grpo_head_merge_partials(const grpo_head_params* p, const void* partials, const float* zy,
+                             const int64_t* y, const uint8_t* mask, float* logp, float* lse,
+                             void* stream) {
+  if (!p) return fail(GRPO_HEAD_INVALID_ARGUMENT, "params is NULL");
+  int rc = check_gemm(p);
+  if (rc) return rc;
+  if (p->n_tokens == 0) return ok();
+  if (!partials || !zy || !y || !logp || !lse)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "a required buffer is NULL");
+  const int64_t n_vt = gh::ceil_div(p->v_real, gh::kVocabTile);
+  gh::MergeArgs ma{(const float2*)partials, zy, y, mask, p->n_tokens, n_vt, p->v_real,
+                   p->ignore_index, logp, lse};
+  hipError_t e = gh::launch_merge(ma, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel");
+  return ok();
+}
 
 int grpo_group_advantage(const float* rewards, int64_t n_seqs, int64_t group_size, float eps,
                          int32_t scale_by_std, float* adv, void* stream) {

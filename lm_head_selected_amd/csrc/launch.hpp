@@ -37,8 +37,9 @@ struct FwdTileArgs {
   float2* partials;  // [n_vt][n_tokens]
   int group_m;
 };
-// Target-logit gather (mode 0: zy[t]) or the backward's target-element fix-up
-// (mode 1: dz[t][y_t] = g_t (1 - p_t,y)); pointers already offset to the chunk.
+// Target-logit gather (mode 0: zy[t]), the backward's target-element fix-up
+// (mode 1: dz[t][y_t] = g_t (1 - p_t,y); pointers already offset to the chunk), or
+// a vocabulary shard's gather (mode 2).
 struct TargetArgs {
   const void* H; const void* W; const int64_t* y; const uint8_t* mask;
   int64_t n_tokens, d_model, v_real, ignore_index;
@@ -47,6 +48,9 @@ struct TargetArgs {
   float* zy;
   const float* lse; const float* coef; const float* grad_output;
   void* dz; int64_t dz_rows;   // dlogits buffer (v-tiled, dz_rows rows per group)
+  // mode 2 (a vocabulary shard's gather): W holds rows [v_begin, v_begin + v_real)
+  // and zy[t] is written for every token, 0 unless y_t lies in the shard
+  int64_t v_begin = 0;
 };
 struct MergeArgs {
   const float2* partials; const float* zy; const int64_t* y; const uint8_t* mask;

@@ -168,3 +168,18 @@ def test_advantage_rejects_bad_arguments(n, G, eps, scale):
 def test_advantage_null_buffers_and_empty():
     assert gb.lib.grpo_group_advantage(None, 8, 4, 0.0, 1, 1, 0) == 1
     assert gb.lib.grpo_group_advantage(None, 0, 4, 0.0, 1, None, 0) == 0   # nothing to do
+
+
+def test_shard_bounds():
+    p = P(v_real=5000, v_rows=5120)
+    N = 1024
+    assert gb.shard_partials_bytes(p, 0, 2560) == 10 * N * 8
+    assert gb.shard_partials_bytes(p, 2560, 5120) == 10 * N * 8    # ragged end: 2440 rows
+    assert gb.shard_partials_bytes(p, 4864, 5001) == 1 * N * 8     # end past v_real
+    for lo, hi in [(100, 2560), (0, 2500), (2560, 2560), (-256, 256), (0, 5121)]:
+        assert gb.shard_partials_bytes(p, lo, hi) == 0, (lo, hi)
+        rc = gb.lib.grpo_head_shard_partials(ctypes.byref(p), lo, hi, 1, 1, 1, None, 1, 1, 0)
+        assert rc == 1
+    q = P(v_real=5000, v_rows=5376)
+    assert gb.shard_partials_bytes(q, 5120, 5376) == 0             # padding only: no tiles
+    assert gb.lib.grpo_head_merge_partials(ctypes.byref(p), None, 1, 1, None, 1, 1, 0) == 1
