@@ -271,6 +271,33 @@ def main():
     torch.cuda.synchronize()
     ms_shard = l0.elapsed_time(l1) / K2
 
+    # gradient-output variants, whole steps: bf16 dH/dW, and dW accumulated into
+    pkw = dict(n_tokens=N, d_model=D, v_real=V, v_rows=cfg.v_rows, n_seqs=inp["n_seqs"],
+               dtype=cfg.dtype, reduction=cfg.reduction, level=cfg.level, inv_tau=cfg.inv_tau,
+               eps_low=cfg.eps_low, eps_high=cfg.eps_high, beta=cfg.beta)
+    p_b16 = gb.make_params(**pkw, grad_dtype="bf16")
+    p_acc = gb.make_params(**pkw, accumulate_dw=True)
+    dH16 = torch.empty(N, D, dtype=torch.bfloat16, device=dev)
+    dW16 = torch.empty(cfg.v_rows, D, dtype=torch.bfloat16, device=dev)
+
+    def variant_ms(pv, dh, dw):
+        def one():
+            head.fwd(d["H"], d["W"], d["y"], d["mask"], d["sid"], d["adv"], d["old"], d["ref"],
+                     stream=stream)
+            gb.grpo_head_bwd(pv, d["H"], d["W"], d["y"], d["mask"], head.lse, head.coef, None,
+                             dh, dw, head.ws, stream=stream)
+        one()
+        torch.cuda.synchronize()
+        l0.record(stream)
+        for _ in range(K2):
+            one()
+        l1.record(stream)
+        torch.cuda.synchronize()
+        return l0.elapsed_time(l1) / K2
+
+    ms_b16 = variant_ms(p_b16, dH16, dW16)
+    ms_acc = variant_ms(p_acc, dH, dW)
+
     stages = {}
     for name, (a, b) in gb.STAGES.items():
         stages[name] = float(np.mean([hev.elapsed_ms(evs[k][a], evs[k][b]) for k in range(K)]))
@@ -312,6 +339,8 @@ def main():
         "logp_entry": {"ms": round(ms_logp, 3), "calls": K2,
                        "tokens_per_s": round(N / (ms_logp / 1e3), 1),
                        "tflops_2nvd": round(2.0 * N * V * D / (ms_logp / 1e3) / 1e12, 1)},
+        "variant_steps_ms": {"bf16_grads": round(ms_b16, 3), "accumulate_dw": round(ms_acc, 3),
+                             "steps": K2},
         "tp2_shard_tiles": {"v_rows": v_half, "ms": round(ms_shard, 3),
                             "tflops": round(2.0 * N * v_half * D / (ms_shard / 1e3) / 1e12, 1)},
     }
