@@ -36,7 +36,8 @@ STAGES = {"fwd_tiles": (0, 1), "fwd_tail": (1, 2), "fwd_objective": (2, 3),
           "bwd_dh": (7, 8), "bwd_dw": (9, 10)}
 # stages that are exactly one matrix-core launch, with that launch's kernel symbol stem
 GEMM_STAGES = {"fwd_tiles": "fwd_tile_kernel", "bwd_dlogits": "dlogits_kernel",
-               "bwd_dh": "product_kernel<__bf16, 0>", "bwd_dw": "product_kernel<__bf16, 1>"}
+               "bwd_dh": "product_kernel<__bf16, 0, float>",
+               "bwd_dw": "product_kernel<__bf16, 1, float>"}
 
 
 class GrpoHeadError(RuntimeError):
