@@ -123,8 +123,9 @@ enum { GRPO_HEAD_LEVEL_TOKEN = 0, GRPO_HEAD_LEVEL_SEQUENCE_GSPO = 1 }; /* p->lev
  *                [1 - eps_low, 1 + eps_high].
  *   beta         KL weight >= 0.  beta > 0 needs ref_logp.
  *   norm_const   fixed_constant only: the divisor C > 0 (finite); ignored otherwise.
- *                The pages name the normaliser without fixing C (Dr. GRPO takes a
- *                constant such as the generation budget times the group size).
+ *                The pages name the normaliser without fixing C (Dr. GRPO, Liu et
+ *                al. 2025, "Understanding R1-Zero-Like Training", divides by a
+ *                constant generation budget).
  *                With fixed_constant a batch without active tokens is not an
  *                error even under validate (same page, review thread on the
  *                zero-active-token guard): the loss is then 0.
