@@ -182,6 +182,49 @@ __device__ __forceinline__ void store_out4(__bf16* p, f32x4 v) {
   __builtin_nontemporal_store(__builtin_bit_cast(i32x2, b), (i32x2*)p);
 }
 
+// The dW tile's epilogue: rows n0 .. n0 + 255 (vocabulary), columns m0 .. m0 + 255
+// (hidden), staged through the (now free) pipeline LDS in two halves of 128 rows
+// and written as whole 1 KB row segments.  16-byte chunk c of LDS row r sits at
+// chunk c ^ (r & 15).  Rows >= zero_from are written as zeros; with accumulate
+// the tile is added to what out holds.
+template <typename O>
+__device__ __forceinline__ void store_dw_tile(const f32x4 (&acc)[kBI][kBJ], char* lds, O* out,
+                                              int64_t ld_out, int64_t n0, int64_t m0,
+                                              int64_t n_limit, int64_t m_limit,
+                                              int64_t zero_from, int accumulate) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / kWN, wn = wave % kWN;
+  float* L = (float*)lds;   // [128][256]
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    if ((wn >> 1) == p) {
+#pragma unroll
+      for (int j = 0; j < kBJ; ++j) {
+        const int r = (wn & 1) * 64 + j * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < kBI; ++i) {
+          const int c = (wm * 128 + i * 16 + (lane >> 4) * 4) >> 2;
+          *(f32x4*)(L + r * 256 + ((c ^ (r & 15)) << 2)) = acc[i][j];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = (threadIdx.x >> 6) + 8 * q, c = threadIdx.x & 63;
+      const int64_t n = n0 + p * 128 + r, m = m0 + c * 4;
+      if (n < n_limit && m < m_limit) {
+        f32x4 v = *(const f32x4*)(L + r * 256 + ((c ^ (r & 15)) << 2));
+        O* o = out + n * ld_out + m;
+        if (n >= zero_from) v = f32x4{0.f, 0.f, 0.f, 0.f};
+        else if (accumulate) v += load_out4(o);
+        store_out4(o, v);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <typename T, int kRole, typename O>
 __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int tiles_m,
                                                            int tiles_n) {
@@ -193,60 +236,29 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
   zero_acc(acc);
   gemm_tile<T, false, true>(a.A, a.B, m0, n0, a.nk, (lds_t*)lds, acc);
 
+  if (kRole == 1) {
+    store_dw_tile<O>(acc, lds, (O*)a.out, a.ld_out, n0, m0, a.n_limit, a.m_limit, a.zero_from,
+                     a.accumulate);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWN, wn = wave % kWN;
   const int64_t mbase = m0 + wm * (kTile / kWM) + (lane >> 4) * 4;
 #pragma unroll
   for (int j = 0; j < kBJ; ++j) {
     const int64_t n = n0 + wn * (kTile / kWN) + j * 16 + (lane & 15);
-    if (kRole == 0) {
-      if (n >= a.n_limit) continue;
-      // 4 consecutive rows m, one column n: a 64-byte run per row across 16 lanes
+    if (n >= a.n_limit) continue;
+    // 4 consecutive rows m, one column n: a 64-byte run per row across 16 lanes
 #pragma unroll
-      for (int i = 0; i < kBI; ++i) {
-        const int64_t m = mbase + i * 16;
+    for (int i = 0; i < kBI; ++i) {
+      const int64_t m = mbase + i * 16;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (m + e >= a.m_limit) continue;
-          O* p = (O*)a.out + (m + e) * a.ld_out + n;
-          const float v = a.accumulate ? acc[i][j][e] + load_out(p) : acc[i][j][e];
-          store_out(p, v);
-        }
+      for (int e = 0; e < 4; ++e) {
+        if (m + e >= a.m_limit) continue;
+        O* p = (O*)a.out + (m + e) * a.ld_out + n;
+        const float v = a.accumulate ? acc[i][j][e] + load_out(p) : acc[i][j][e];
+        store_out(p, v);
       }
-    }
-  }
-  if (kRole == 1) {
-    // dW rows n0 .. n0 + 255, columns m0 .. m0 + 255: staged through LDS (free
-    // now) in two halves of 128 rows, then written as whole 1 KB row segments.
-    // 16-byte chunk c of LDS row r sits at chunk c ^ (r & 15).
-    float* L = (float*)lds;   // [128][256]
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      if ((wn >> 1) == p) {
-#pragma unroll
-        for (int j = 0; j < kBJ; ++j) {
-          const int r = (wn & 1) * 64 + j * 16 + (lane & 15);
-#pragma unroll
-          for (int i = 0; i < kBI; ++i) {
-            const int c = (wm * 128 + i * 16 + (lane >> 4) * 4) >> 2;
-            *(f32x4*)(L + r * 256 + ((c ^ (r & 15)) << 2)) = acc[i][j];
-          }
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r = (threadIdx.x >> 6) + 8 * q, c = threadIdx.x & 63;
-        const int64_t n = n0 + p * 128 + r, m = m0 + c * 4;
-        if (n < a.n_limit && m < a.m_limit) {
-          f32x4 v = *(const f32x4*)(L + r * 256 + ((c ^ (r & 15)) << 2));
-          O* o = (O*)a.out + n * a.ld_out + m;
-          if (n >= a.zero_from) v = f32x4{0.f, 0.f, 0.f, 0.f};
-          else if (a.accumulate) v += load_out4(o);
-          store_out4(o, v);
-        }
-      }
-      __syncthreads();
     }
   }
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tile_order.hpp"
+
 namespace gh {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -41,25 +43,5 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 template <typename T> struct Elem;
 template <> struct Elem<__bf16> { static constexpr int size = 2; };
 template <> struct Elem<float> { static constexpr int size = 4; };
-
-// XCD-aware tile order.  Workgroups are dispatched round-robin over the 8 XCDs
-// (bid % 8).  Renumber so each XCD receives a contiguous run of logical tile ids;
-// inside a run, tiles walk `group_m` M-tiles down one N-tile before moving to the
-// next N-tile, so workgroups resident together on one XCD share operand slices
-// in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_m, int tiles_n,
-                                            int group_m, int& tm, int& tn) {
-  const int q = nwg >> 3, r = nwg & 7;
-  const int xcd = bid & 7, idx = bid >> 3;
-  const int logical = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-  const int per_group = group_m * tiles_n;
-  const int g = logical / per_group;
-  const int first_m = g * group_m;
-  int gsize = tiles_m - first_m;
-  gsize = gsize < group_m ? gsize : group_m;
-  const int in_g = logical - g * per_group;
-  tm = first_m + in_g % gsize;
-  tn = in_g / gsize;
-}
 
 }  // namespace gh

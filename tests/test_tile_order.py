@@ -1,0 +1,67 @@
+"""The matrix-core launches' tile order (csrc/tile_order.hpp) compiled on the host
+with g++: every workgroup-to-tile mapping is a bijection onto the tile grid, and a
+launch of fewer workgroups covers exactly the first logical ids."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from tests.conftest import ROOT
+
+HDR = os.path.join(ROOT, "lm_head_selected_amd", "csrc")
+
+DRIVER = r"""
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+#include "tile_order.hpp"
+int main(int argc, char** argv) {
+  const int tm_ = atoi(argv[1]), tn_ = atoi(argv[2]), g = atoi(argv[3]), nwg = atoi(argv[4]);
+  std::vector<int> seen(tm_ * tn_, 0), logical(nwg, 0);
+  for (int b = 0; b < nwg; ++b) {
+    const int l = gh::xcd_logical(b, nwg);
+    if (l < 0 || l >= nwg) { printf("logical out of range\n"); return 1; }
+    logical[l]++;
+    int m, n;
+    gh::tile_coords(b, nwg, tm_, tn_, g, m, n);
+    if (m < 0 || m >= tm_ || n < 0 || n >= tn_) { printf("tile out of range\n"); return 1; }
+    seen[m * tn_ + n]++;
+  }
+  for (int l = 0; l < nwg; ++l) if (logical[l] != 1) { printf("logical not a bijection\n"); return 1; }
+  // the tail (ids nwg .. total-1) mapped directly completes the grid exactly once
+  for (int l = nwg; l < tm_ * tn_; ++l) {
+    int m, n;
+    gh::logical_coords(l, tm_, tn_, g, m, n);
+    seen[m * tn_ + n]++;
+  }
+  for (int i = 0; i < tm_ * tn_; ++i) if (seen[i] != 1) { printf("tile %d seen %d\n", i, seen[i]); return 1; }
+  printf("ok\n");
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    d = tmp_path_factory.mktemp("tile_order")
+    src = d / "driver.cpp"
+    src.write_text(DRIVER)
+    exe = d / "driver"
+    subprocess.run([gxx, "-std=c++17", "-O1", "-DGH_HOST_DEVICE=", f"-I{HDR}", str(src), "-o",
+                    str(exe)], check=True)
+    return str(exe)
+
+
+@pytest.mark.parametrize("tm,tn,g,frac", [
+    (594, 32, 8, 1.0), (594, 64, 4, 1.0), (32, 16, 4, 1.0), (16, 594, 4, 1.0),
+    (16, 594, 4, 9472 / 9504), (16, 20, 4, 1.0), (1, 2, 8, 1.0), (7, 3, 4, 1.0),
+    (13, 11, 8, 0.5), (594, 32, 8, 0.9)])
+def test_tile_order_is_a_bijection(driver, tm, tn, g, frac):
+    nwg = max(1, int(round(tm * tn * frac)))
+    out = subprocess.run([driver, str(tm), str(tn), str(g), str(nwg)], capture_output=True,
+                         text=True)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
