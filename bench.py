@@ -211,6 +211,11 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the backward runs on the tokens whose gradient scale is non-zero (grad_output
+    # = 1): active tokens with coef != 0; the others' dlogits rows are all zero
+    coef_h = head.coef.cpu().numpy()
+    active = (inp["mask"] != 0) if inp["mask"] is not None else (inp["y"] != inp["ignore_index"])
+    n_live = int(np.count_nonzero(active & (coef_h != 0.0)))
 
     K = args.steps
     hev = HipEvents()
@@ -304,9 +309,10 @@ def main():
     per_step = [hev.elapsed_ms(evs[k][0], evs[k][gb.N_STAGE_EVENTS - 1]) for k in range(K)]
     hev.destroy()
 
-    # algorithmic flops of each matrix-core launch: 2 N D V (real vocabulary rows)
-    launch_flops = {"fwd_tiles": 2.0 * N * D * V, "bwd_dlogits": 2.0 * N * D * V,
-                    "bwd_dh": 2.0 * N * D * V, "bwd_dw": 2.0 * N * D * V}
+    # algorithmic flops of each matrix-core launch: 2 D V (real vocabulary rows) per
+    # row it processes: every token in the forward, the live rows in the backward
+    launch_flops = {"fwd_tiles": 2.0 * N * D * V, "bwd_dlogits": 2.0 * n_live * D * V,
+                    "bwd_dh": 2.0 * n_live * D * V, "bwd_dw": 2.0 * n_live * D * V}
     gemm = {s: {"ms": round(stages[s], 3),
                 "tflops": round(launch_flops[s] / (stages[s] / 1e3) / 1e12, 1)}
             for s in gb.GEMM_STAGES}
@@ -319,6 +325,7 @@ def main():
                 "flops_per_launch": launch_flops[dom], "launch_ms": round(stages[dom], 3)}
 
     flops_8nvd = 8.0 * N * V * D
+    flops_exec = (2.0 * N + 6.0 * n_live) * V * D
     out = {
         "metric": "tokens/s fwd+bwd fused GRPO head loss + % bf16 MFMA peak, D=4096 V=151936",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -332,6 +339,9 @@ def main():
         "tflops_8nvd": round(flops_8nvd / (ms_step / 1e3) / 1e12, 1),
         "tflops_6nvd": round(0.75 * flops_8nvd / (ms_step / 1e3) / 1e12, 1),
         "frac_of_peak_8nvd": round(flops_8nvd / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "backward_rows": n_live,
+        "tflops_executed": round(flops_exec / (ms_step / 1e3) / 1e12, 1),
+        "frac_of_peak_executed": round(flops_exec / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "gemm_launches": gemm,
         "stages_ms": {k: round(v, 3) for k, v in stages.items()},
         "wall_s": round(wall, 3),

@@ -166,8 +166,8 @@ typedef struct grpo_head_params {
 size_t grpo_head_fwd_workspace_size(const grpo_head_params* p);
 
 /* Bytes of device workspace grpo_head_bwd needs (the bf16 or fp32 dlogits of one
- * token chunk over the 256-padded vocabulary, the chunk's hidden states
- * transposed, and per-token scalars); also at
+ * token chunk over the 256-padded vocabulary, the chunk's gathered hidden states
+ * as rows and transposed, and per-token scalars and row indices); also at
  * least grpo_head_fwd_workspace_size(p), so one buffer serves all calls.
  * 0 if p is invalid. */
 size_t grpo_head_workspace_size(const grpo_head_params* p);
@@ -200,7 +200,11 @@ int grpo_head_fwd(const grpo_head_params* p, const void* H, const void* W, const
  * dH is overwritten.  dW is overwritten, or with p->accumulate_dw the gradient
  * is added to it (rows [0, v_real) only; the padding rows are not touched).
  * Token chunks are processed in ascending order and dW accumulates them in that
- * order.  dH and dW hold fp32 or bf16 elements (p->grad_dtype).
+ * order.  Within a chunk only the tokens with a non-zero scale
+ * grad_output * coef[t] * inv_tau reach the matrix-core products, in ascending
+ * token order (their G rows are the only non-zero ones); the other tokens' dH
+ * rows are written as zeros.  dH and dW hold fp32 or bf16 elements
+ * (p->grad_dtype).
  * Status 0, 1, 2, 6; with validate also 4 (active target out of range) and 5
  * (non-finite lse or coef). */
 int grpo_head_bwd(const grpo_head_params* p, const void* H, const void* W, const int64_t* y,

@@ -6,15 +6,23 @@
 // thread on the saved fp32 logits; here the logits are recomputed per tile rather
 // than saved).  Inactive tokens give 0.
 //
+// A token whose scale g_t = grad_output * coef_t / tau is zero (an inactive token,
+// or a clipped one with no KL term) has an all-zero dlogits row: it adds nothing to
+// dW and its dH row is zero.  The backward therefore runs on the chunk's live rows
+// only, compacted in token order.  Their count stays on the device: each launch
+// reads it and sizes its tile walk or K loop from it, so nothing waits on the host.
+//
 // Per token chunk, in ascending chunk order:
-//   1. dlogits_prep_kernel: (g_t, lse_t log2 e) per token
-//   2. dlogits_kernel     : -g_t p_tv tile on the matrix cores -> dz (bf16, nearest
+//   1. live_count_kernel, compact_kernel: the live tokens in ascending order
+//      (rows[r] = token, rowpos[t] = r or -1), their (g_t, lse_t log2 e), the count
+//   2. gather_rows_kernel : the live H rows, as Hg[r][d] and transposed HT[d][r]
+//      zero_dead_rows_kernel: dH rows of the dead tokens = 0
+//   3. dlogits_kernel     : -g_t p_tv tile on the matrix cores -> dz (bf16, nearest
 //                           even, on the bf16 path; fp32 on the fp32 path)
-//      target_logit_kernel: rewrites dz[t][y_t] = g_t (1 - p_t,y_t)
-//   3. product_kernel<0>  : dH[t][d] = sum_v dz[t][v] W[v][d]
-//      (M = t: dz K-contiguous; N = d: W read MN-contiguous)
-//   4. transpose_kernel   : HT[d][t] of the chunk (small: D x chunk)
-//   5. product_kernel<1>  : dW[v][d] (+)= sum_t HT[d][t] dz[t][v]
+//      target_logit_kernel: rewrites dz[r][y_t] = g_t (1 - p_t,y_t)
+//   4. product_kernel<0>  : dH[rows[r]][d] = sum_v dz[r][v] W[v][d]
+//      (M = r: dz K-contiguous; N = d: W read MN-contiguous)
+//   5. product_kernel<1>  : dW[v][d] (+)= sum_r HT[d][r] dz[r][v]
 //      (M = d: HT K-contiguous; N = v: dz read MN-contiguous)
 // W and dz are read where they are; the tile core forms the transposed MFMA
 // fragments of the MN-contiguous operand with the gfx950 transposing LDS read,
@@ -52,28 +60,92 @@ template <> struct Store4<float> {
 };
 
 struct DlogitsArgs {
-  const void* W; const void* H;   // H already offset to the chunk's first token
-  const float2* gl;               // per chunk token: (g_t, lse_t * log2 e); g_t = 0 if inactive
-  int64_t chunk_tokens;           // valid tokens in this chunk
+  const void* W; const void* H;   // H: the chunk's live rows (Hg)
+  const float2* gl;               // per row: (g_t, lse_t * log2 e); (0, 0) past the live rows
+  int64_t chunk_tokens;           // rows of H and gl inside the chunk
   int64_t d_model, v_real;
   float inv_tau;
   void* dz;                       // v-tiled [n_vt][dz_rows][256]
   int64_t dz_rows;
   int group_m;
+  const int32_t* live;            // live row count (device); token tiles past it are skipped
 };
 
-// g_t = grad_output * coef_t / tau for active tokens (0 otherwise) and lse_t in
-// base-2 units, for the chunk's tokens.
-__global__ __launch_bounds__(256) void dlogits_prep_kernel(const int64_t* y, const uint8_t* mask,
-                                                           int64_t ignore_index, const float* coef,
-                                                           const float* lse,
-                                                           const float* grad_output, float inv_tau,
-                                                           int64_t n, float2* gl) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n) return;
-  const bool act = token_is_active(mask, y, ignore_index, t);
-  const float gout = grad_output ? *grad_output : 1.0f;
-  gl[t] = make_float2(act ? gout * coef[t] * inv_tau : 0.0f, lse[t] * kLog2e);
+// Row compaction of one chunk (blocks of kCompactBlock tokens, one per thread).
+struct CompactArgs {
+  const int64_t* y; const uint8_t* mask; int64_t ignore_index;
+  const float* coef; const float* lse; const float* grad_output; float inv_tau;
+  int64_t n;          // tokens of the chunk
+  int64_t n_pad;      // rows of the compact buffers
+  int32_t* bcnt;      // [blocks] live tokens per block
+  int32_t* live;      // live tokens of the chunk
+  int32_t* rows;      // [n_pad] token of compact row r (-1 past the live rows)
+  int32_t* rowpos;    // [n] compact row of token t, -1 if dead
+  float2* gl;         // [n_pad] (g_t, lse_t log2 e) of compact row r; (0, 0) past them
+};
+
+// g_t = grad_output * coef_t / tau for an active token, 0 otherwise.  A token is
+// live when g_t != 0 (a NaN scale stays live, so it reaches the gradients).
+__device__ __forceinline__ float grad_scale(const CompactArgs& a, int64_t t) {
+  const bool act = token_is_active(a.mask, a.y, a.ignore_index, t);
+  const float gout = a.grad_output ? *a.grad_output : 1.0f;
+  return act ? gout * a.coef[t] * a.inv_tau : 0.0f;
+}
+
+constexpr int kCompactWaves = (int)kCompactBlock / 64;
+
+__global__ __launch_bounds__(kCompactBlock) void live_count_kernel(CompactArgs a) {
+  __shared__ int wcnt[kCompactWaves];
+  const int64_t t = (int64_t)blockIdx.x * kCompactBlock + threadIdx.x;
+  const bool lv = t < a.n && grad_scale(a, t) != 0.0f;
+  const uint64_t b = __ballot(lv);
+  if ((threadIdx.x & 63) == 0) wcnt[threadIdx.x >> 6] = __popcll(b);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int c = 0;
+    for (int w = 0; w < kCompactWaves; ++w) c += wcnt[w];
+    a.bcnt[blockIdx.x] = c;
+  }
+}
+
+// Each block places its live tokens after those of the blocks before it, in token
+// order; the last block also writes the count and clears the rows past it.
+__global__ __launch_bounds__(kCompactBlock) void compact_kernel(CompactArgs a) {
+  __shared__ int wcnt[kCompactWaves];
+  __shared__ int base;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    int c = 0;
+    for (int b = lane; b < (int)blockIdx.x; b += 64) c += a.bcnt[b];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    if (lane == 0) base = c;
+  }
+  const int64_t t = (int64_t)blockIdx.x * kCompactBlock + threadIdx.x;
+  const float g = t < a.n ? grad_scale(a, t) : 0.0f;
+  const bool lv = t < a.n && g != 0.0f;
+  const uint64_t b = __ballot(lv);
+  if (lane == 0) wcnt[wave] = __popcll(b);
+  __syncthreads();
+  int pos = base;
+  for (int w = 0; w < wave; ++w) pos += wcnt[w];
+  pos += __popcll(b & ((uint64_t(1) << lane) - 1));
+  if (t < a.n) {
+    a.rowpos[t] = lv ? pos : -1;
+    if (lv) {
+      a.rows[pos] = (int32_t)t;
+      a.gl[pos] = make_float2(g, a.lse[t] * kLog2e);
+    }
+  }
+  if (blockIdx.x == gridDim.x - 1) {
+    int total = base;
+    for (int w = 0; w < kCompactWaves; ++w) total += wcnt[w];
+    if (threadIdx.x == 0) *a.live = total;
+    for (int64_t r = total + threadIdx.x; r < a.n_pad; r += kCompactBlock) {
+      a.rows[r] = -1;
+      a.gl[r] = make_float2(0.0f, 0.0f);
+    }
+  }
 }
 
 // dz[t][v] = -g_t p_tv over the tile (the target element is rewritten afterwards
@@ -84,8 +156,12 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int tiles_m,
                                                            int tiles_n) {
   __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+  // the launch covers every token tile of the chunk; only those holding live rows run
+  const int live_n = (int)ceil_div((int64_t)*a.live, kTile);
+  const int nwg = tiles_m * (live_n < tiles_n ? live_n : tiles_n);
+  if ((int)blockIdx.x >= nwg) return;
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, a.group_m, tm, tn);
+  tile_coords(blockIdx.x, nwg, tiles_m, live_n < tiles_n ? live_n : tiles_n, a.group_m, tm, tn);
   const int64_t v0 = (int64_t)tm * kTile, t0 = (int64_t)tn * kTile;
   const int64_t esz = Elem<T>::size;
   const Operand A = nt_row_major(a.W, a.d_model * esz, a.v_real);
@@ -159,6 +235,11 @@ struct ProductArgs {
   int64_t zero_from;              // dW rows (N) >= this are written as 0 (padded vocab)
   int accumulate;                 // add to out
   int group_m;
+  // live row count (device): kRole 0 runs the M tiles holding live rows and
+  // writes compact row m to out row out_rows[m]; kRole 1 runs the K stages
+  // covering them
+  const int32_t* live;
+  const int32_t* out_rows;
 };
 
 // Output element stores: fp32, or bf16 rounded to nearest even.
@@ -229,15 +310,28 @@ template <typename T, int kRole, typename O>
 __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int tiles_m,
                                                            int tiles_n) {
   __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+  const int64_t na = *a.live;
+  int nwg = (int)gridDim.x, nk = a.nk;
+  int64_t m_limit = a.m_limit;
+  if (kRole == 0) {
+    const int live_m = (int)ceil_div(na, kTile);
+    if (live_m < tiles_m) tiles_m = live_m;
+    nwg = tiles_m * tiles_n;
+    if ((int)blockIdx.x >= nwg) return;
+    if (na < m_limit) m_limit = na;
+  } else {
+    const int live_k = (int)ceil_div(na * (int64_t)sizeof(T), kStageBytes);
+    if (live_k < nk) nk = live_k;
+  }
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, a.group_m, tm, tn);
+  tile_coords(blockIdx.x, nwg, tiles_m, tiles_n, a.group_m, tm, tn);
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
   f32x4 acc[kBI][kBJ];
   zero_acc(acc);
-  gemm_tile<T, false, true>(a.A, a.B, m0, n0, a.nk, (lds_t*)lds, acc);
+  gemm_tile<T, false, true>(a.A, a.B, m0, n0, nk, (lds_t*)lds, acc);
 
   if (kRole == 1) {
-    store_dw_tile<O>(acc, lds, (O*)a.out, a.ld_out, n0, m0, a.n_limit, a.m_limit, a.zero_from,
+    store_dw_tile<O>(acc, lds, (O*)a.out, a.ld_out, n0, m0, a.n_limit, m_limit, a.zero_from,
                      a.accumulate);
     return;
   }
@@ -254,8 +348,10 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
       const int64_t m = mbase + i * 16;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (m + e >= a.m_limit) continue;
-        O* p = (O*)a.out + (m + e) * a.ld_out + n;
+        if (m + e >= m_limit) continue;
+        const int64_t row = a.out_rows[m + e];
+        if (row < 0) continue;
+        O* p = (O*)a.out + row * a.ld_out + n;
         const float v = a.accumulate ? acc[i][j][e] + load_out(p) : acc[i][j][e];
         store_out(p, v);
       }
@@ -263,25 +359,48 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
   }
 }
 
-// HT[d][t] = H[t][d] for t < rows, 0 for rows <= t < rows_pad; HT rows are
-// ld_out elements long.  64 x 64 element tiles through LDS.
+// The chunk's live H rows, Hg[r][d] = H[rows[r]][d] and HT[d][r] (HT rows are
+// ld_out elements long), zero for rows[r] past the live count.  Only the rows the
+// products read are written: those of token tiles holding live rows.  64 x 64
+// element tiles through LDS.
 template <typename E>
-__global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ H, int64_t d_model,
-                                                        int64_t rows, E* __restrict__ HT,
-                                                        int64_t ld_out, int tiles_d) {
+__global__ __launch_bounds__(256) void gather_rows_kernel(const E* __restrict__ H,
+                                                          int64_t d_model,
+                                                          const int32_t* __restrict__ rows,
+                                                          const int32_t* live, E* __restrict__ Hg,
+                                                          E* __restrict__ HT, int64_t ld_out,
+                                                          int tiles_d) {
   __shared__ E tile[64][65];
-  const int64_t td = blockIdx.x % tiles_d, tt = blockIdx.x / tiles_d;
-  const int64_t d0 = td * 64, t0 = tt * 64;
+  const int64_t td = blockIdx.x % tiles_d, tr = blockIdx.x / tiles_d;
+  const int64_t d0 = td * 64, r0 = tr * 64;
+  const int64_t na = *live;
+  if (r0 >= ceil_div(na, kTile) * kTile) return;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int k = ty; k < 64; k += 4) {
-    const int64_t t = t0 + k, d = d0 + tx;
-    tile[k][tx] = (t < rows && d < d_model) ? H[t * d_model + d] : E(0);
+    const int64_t r = r0 + k, d = d0 + tx;
+    if (d >= d_model) continue;
+    const int64_t src = r < na ? rows[r] : -1;
+    const E v = src >= 0 ? H[src * d_model + d] : E(0);
+    tile[k][tx] = v;
+    Hg[r * d_model + d] = v;
   }
   __syncthreads();
   for (int k = ty; k < 64; k += 4) {
-    const int64_t d = d0 + k, t = t0 + tx;
-    if (d < d_model) HT[d * ld_out + t] = tile[tx][k];
+    const int64_t d = d0 + k, r = r0 + tx;
+    if (d < d_model) HT[d * ld_out + r] = tile[tx][k];
   }
+}
+
+// dH rows of the chunk's dead tokens are zero (no product tile reaches them).
+// One wave per token.
+template <typename O>
+__global__ __launch_bounds__(256) void zero_dead_rows_kernel(const int32_t* __restrict__ rowpos,
+                                                             int64_t n, int64_t d_model,
+                                                             O* __restrict__ dH) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= n || rowpos[t] >= 0) return;
+  O* row = dH + t * d_model;
+  for (int64_t d = threadIdx.x & 63; d < d_model; d += 64) row[d] = (O)0.0f;
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, int64_t words) {
@@ -324,50 +443,63 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
 
   const int tiles_v = (int)L.n_vt;
   const int tiles_d = (int)ceil_div(D, kTile);
+  int32_t* bcnt = (int32_t*)(a.ws + L.bcnt);
+  int32_t* live = (int32_t*)(a.ws + L.live);
+  int32_t* rows = (int32_t*)(a.ws + L.rows);
+  int32_t* rowpos = (int32_t*)(a.ws + L.rowpos);
+  char* hg = a.ws + L.hg;
+  typedef typename std::conditional<sizeof(T) == 2, uint16_t, float>::type E;
   for (int64_t c0 = 0; c0 < N; c0 += R) {
     const int64_t nc = (N - c0) < R ? (N - c0) : R;
     const int64_t ncp = ceil_div(nc, kTokenTile) * kTokenTile;
     const int tiles_t = (int)(ncp / kTokenTile);
     const char* Hc = (const char*)a.H + c0 * D * esz;
-
     const uint8_t* cmask = a.mask ? a.mask + c0 : nullptr;
-    hipLaunchKernelGGL(dlogits_prep_kernel, dim3((unsigned)ceil_div(nc, 256)), dim3(256), 0, s,
-                       a.y + c0, cmask, a.ignore_index, a.coef + c0, a.lse + c0, a.grad_output,
-                       a.inv_tau, nc, gl);
-    DlogitsArgs d{a.W, Hc, gl, nc, D, a.v_real, a.inv_tau, dz, R, a.group_fwd};
+
+    // live rows of the chunk, their H rows, and zero dH rows for the dead tokens
+    const CompactArgs ca{a.y + c0, cmask, a.ignore_index, a.coef + c0, a.lse + c0, a.grad_output,
+                         a.inv_tau, nc, ncp, bcnt, live, rows, rowpos, gl};
+    const unsigned nb = (unsigned)ceil_div(nc, kCompactBlock);
+    hipLaunchKernelGGL(live_count_kernel, dim3(nb), dim3(kCompactBlock), 0, s, ca);
+    hipLaunchKernelGGL(compact_kernel, dim3(nb), dim3(kCompactBlock), 0, s, ca);
+    const int ttd = (int)ceil_div(D, 64);
+    hipLaunchKernelGGL(gather_rows_kernel<E>, dim3((unsigned)(ttd * (ncp / 64))), dim3(256), 0, s,
+                       (const E*)Hc, D, (const int32_t*)rows, (const int32_t*)live, (E*)hg,
+                       (E*)ht, R, ttd);
+    hipLaunchKernelGGL(zero_dead_rows_kernel<O>, dim3((unsigned)ceil_div(nc, 4)), dim3(256), 0, s,
+                       (const int32_t*)rowpos, nc, D, dH + c0 * D);
+
+    DlogitsArgs d{a.W, hg, gl, nc, D, a.v_real, a.inv_tau, dz, R, a.group_fwd, live};
     ev.mark(5, s);
     hipLaunchKernelGGL(dlogits_kernel<T>, dim3(tiles_v * tiles_t), dim3(kThreads), 0, s, d,
                        tiles_v, tiles_t);
     ev.mark(6, s);
     TargetArgs fx{Hc, a.W, a.y + c0, cmask, nc, D, a.v_real, a.ignore_index, a.inv_tau, 1,
                   nullptr, a.lse + c0, a.coef + c0, a.grad_output, dz, R};
+    fx.rows = rows;
+    fx.live = live;
     hipError_t e0 = launch_target_logit(sizeof(T) == 2 ? 0 : 1, fx, s);
     if (e0 != hipSuccess) return e0;
     ev.mark(7, s);
 
-    // dH rows of the chunk: M = t (dz rows), N = d (W read MN-contiguous), K = v.
-    // W rows >= v_real are never read (they load as zeros).
+    // dH rows of the chunk: M = live row r (dz rows), N = d (W read MN-contiguous),
+    // K = v; row r goes to token rows[r].  W rows >= v_real are never read (they
+    // load as zeros).
     ProductArgs ph{nt_vtiled(dz, R, esz, (int64_t)tiles_v * R * 256 * esz),
                    mn_row_major(a.W, D * esz, a.v_real, D, esz), (int)(VK * esz / kStageBytes),
-                   dH + c0 * D, D, nc, D, INT64_MAX, 0, a.group_dh};
+                   dH + c0 * D, D, nc, D, INT64_MAX, 0, a.group_dh, live, rows};
     hipLaunchKernelGGL((product_kernel<T, 0, O>), dim3(tiles_t * tiles_d), dim3(kThreads), 0, s,
                        ph, tiles_t, tiles_d);
     ev.mark(8, s);
-
-    // HT of the chunk: D rows of ncp tokens (zero past nc)
-    typedef typename std::conditional<sizeof(T) == 2, uint16_t, float>::type E;
-    const int ttd = (int)ceil_div(D, 64);
-    hipLaunchKernelGGL(transpose_kernel<E>, dim3((unsigned)(ttd * (ncp / 64))), dim3(256), 0, s,
-                       (const E*)Hc, D, nc, (E*)ht, R, ttd);
     ev.mark(9, s);
 
-    // dW: M = d (HT K-contiguous), N = v (dz read MN-contiguous), K = t.  Rows
-    // [v_real, VK) of the last tile are written as zeros, or, when accumulating
-    // into the caller's dW, not written at all.
+    // dW: M = d (HT K-contiguous), N = v (dz read MN-contiguous), K = live row.
+    // Rows [v_real, VK) of the last tile are written as zeros, or, when
+    // accumulating into the caller's dW, not written at all.
     ProductArgs pw{nt_row_major(ht, R * esz, D), mn_vtiled(dz, R, esz, tiles_v),
                    (int)(ncp * esz / kStageBytes), dW, D, D,
                    a.accumulate_dw ? a.v_real : (a.v_rows < VK ? a.v_rows : VK), a.v_real,
-                   (c0 > 0 || a.accumulate_dw) ? 1 : 0, a.group_dw};
+                   (c0 > 0 || a.accumulate_dw) ? 1 : 0, a.group_dw, live, nullptr};
     hipLaunchKernelGGL((product_kernel<T, 1, O>), dim3(tiles_d * tiles_v), dim3(kThreads), 0, s,
                        pw, tiles_d, tiles_v);
     ev.mark(10, s);

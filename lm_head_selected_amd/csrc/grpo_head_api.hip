@@ -137,7 +137,12 @@ gh::WsLayout layout(const grpo_head_params* p, bool with_gemm = true) {
   L.bflags = take(64);
   L.gl = take((size_t)chunk * 8);
   L.dz = take((size_t)chunk * L.v_k * esz);   // dlogits of one chunk, v-tiled
-  L.ht = take((size_t)D * chunk * esz);       // the chunk's H transposed
+  L.ht = take((size_t)D * chunk * esz);       // the chunk's live H rows transposed
+  L.bcnt = take((size_t)gh::ceil_div(chunk, gh::kCompactBlock) * 4);
+  L.live = take(4);
+  L.rows = take((size_t)chunk * 4);
+  L.rowpos = take((size_t)chunk * 4);
+  L.hg = take((size_t)chunk * D * esz);       // the chunk's live H rows
   L.bwd_bytes = off > L.fwd_bytes ? off : L.fwd_bytes;
   return L;
 }
@@ -247,7 +252,7 @@ int check_shard(const grpo_head_params* p, int64_t v_begin, int64_t v_end, int64
   if (v_begin % gh::kVocabTile != 0 || (v_end % gh::kVocabTile != 0 && v_end < p->v_real))
     return fail(GRPO_HEAD_INVALID_ARGUMENT,
                 "shard bounds must lie on the %d-row tile grid (or the end at or past v_real)",
-                gh::kVocabTile);
+                (int)gh::kVocabTile);
   const int64_t hi = v_end < p->v_real ? v_end : p->v_real;
   *real_rows = hi > v_begin ? hi - v_begin : 0;
   return GRPO_HEAD_OK;

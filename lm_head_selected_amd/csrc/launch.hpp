@@ -9,9 +9,10 @@ namespace gh {
 
 constexpr int64_t kVocabTile = 256;   // vocabulary rows per forward/backward tile
 constexpr int64_t kTokenTile = 256;   // tokens per tile
+constexpr int64_t kCompactBlock = 1024;  // tokens per block of the backward row compaction
 constexpr size_t kAlign = 256;
 
-inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Byte offsets into the caller's workspace.
@@ -21,6 +22,9 @@ struct WsLayout {
   size_t fwd_bytes = 0;
   // backward (reuses the workspace from offset 0)
   size_t bflags = 0, gl = 0, dz = 0, ht = 0;
+  // backward row compaction: per-block live counts, the live count, the live rows'
+  // token indices, every token's compact row (-1 if dead) and the gathered H rows
+  size_t bcnt = 0, live = 0, rows = 0, rowpos = 0, hg = 0;
   size_t bwd_bytes = 0;
   int64_t n_vt = 0;        // vocabulary tiles covering [0, v_real)
   int64_t v_k = 0;         // n_vt * 256: vocabulary extent of the dlogits buffer
@@ -51,6 +55,8 @@ struct TargetArgs {
   // mode 2 (a vocabulary shard's gather): W holds rows [v_begin, v_begin + v_real)
   // and zy[t] is written for every token, 0 unless y_t lies in the shard
   int64_t v_begin = 0;
+  // mode 1 on compacted rows: dz row r < *live holds token rows[r] (else dz row = t)
+  const int32_t* rows = nullptr; const int32_t* live = nullptr;
 };
 struct MergeArgs {
   const float2* partials; const float* zy; const int64_t* y; const uint8_t* mask;
