@@ -311,8 +311,9 @@ def main():
 
     # algorithmic flops of each matrix-core launch: 2 D V (real vocabulary rows) per
     # row it processes: every token in the forward, the live rows in the backward
+    # (the gradient launch runs both products, dH and dW: twice that)
     launch_flops = {"fwd_tiles": 2.0 * N * D * V, "bwd_dlogits": 2.0 * n_live * D * V,
-                    "bwd_dh": 2.0 * n_live * D * V, "bwd_dw": 2.0 * n_live * D * V}
+                    "bwd_grads": 4.0 * n_live * D * V}
     gemm = {s: {"ms": round(stages[s], 3),
                 "tflops": round(launch_flops[s] / (stages[s] / 1e3) / 1e12, 1)}
             for s in gb.GEMM_STAGES}

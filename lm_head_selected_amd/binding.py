@@ -30,14 +30,13 @@ EXPORTS = ("grpo_head_fwd_workspace_size", "grpo_head_workspace_size",
            "grpo_head_merge_partials", "grpo_head_set_stage_events", "grpo_head_last_error")
 
 # stage-event slots recorded by grpo_head_fwd / grpo_head_bwd
-N_STAGE_EVENTS = 11
+N_STAGE_EVENTS = 9
 STAGES = {"fwd_tiles": (0, 1), "fwd_tail": (1, 2), "fwd_objective": (2, 3),
           "bwd_prep": (4, 5), "bwd_dlogits": (5, 6), "bwd_target": (6, 7),
-          "bwd_dh": (7, 8), "bwd_dw": (9, 10)}
+          "bwd_grads": (7, 8)}
 # stages that are exactly one matrix-core launch, with that launch's kernel symbol stem
 GEMM_STAGES = {"fwd_tiles": "fwd_tile_kernel", "bwd_dlogits": "dlogits_kernel",
-               "bwd_dh": "product_kernel<__bf16, 0, float>",
-               "bwd_dw": "product_kernel<__bf16, 1, float>"}
+               "bwd_grads": "grad_products_kernel<__bf16, float>"}
 
 
 class GrpoHeadError(RuntimeError):

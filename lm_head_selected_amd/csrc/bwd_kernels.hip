@@ -20,9 +20,10 @@
 //   3. dlogits_kernel     : -g_t p_tv tile on the matrix cores -> dz (bf16, nearest
 //                           even, on the bf16 path; fp32 on the fp32 path)
 //      target_logit_kernel: rewrites dz[r][y_t] = g_t (1 - p_t,y_t)
-//   4. product_kernel<0>  : dH[rows[r]][d] = sum_v dz[r][v] W[v][d]
-//      (M = r: dz K-contiguous; N = d: W read MN-contiguous)
-//   5. product_kernel<1>  : dW[v][d] (+)= sum_r HT[d][r] dz[r][v]
+//   4. grad_products_kernel, one launch of two products:
+//      dH[rows[r]][d] = sum_v dz[r][v] W[v][d]
+//      (M = r: dz K-contiguous; N = d: W read MN-contiguous), and
+//      dW[v][d] (+)= sum_r HT[d][r] dz[r][v]
 //      (M = d: HT K-contiguous; N = v: dz read MN-contiguous)
 // W and dz are read where they are; the tile core forms the transposed MFMA
 // fragments of the MN-contiguous operand with the gfx950 transposing LDS read,
@@ -306,25 +307,26 @@ __device__ __forceinline__ void store_dw_tile(const f32x4 (&acc)[kBI][kBJ], char
   }
 }
 
+// One output tile of a gradient product: workgroup `bid` of the `nwg` the product
+// was given (kRole 0 runs only the tiles holding live rows and lets the rest go).
 template <typename T, int kRole, typename O>
-__global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int tiles_m,
-                                                           int tiles_n) {
-  __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+__device__ __forceinline__ void product_tile(const ProductArgs& a, int bid, int nwg, int tiles_m,
+                                             int tiles_n, char* lds) {
   const int64_t na = *a.live;
-  int nwg = (int)gridDim.x, nk = a.nk;
+  int nk = a.nk;
   int64_t m_limit = a.m_limit;
   if (kRole == 0) {
     const int live_m = (int)ceil_div(na, kTile);
     if (live_m < tiles_m) tiles_m = live_m;
     nwg = tiles_m * tiles_n;
-    if ((int)blockIdx.x >= nwg) return;
+    if (bid >= nwg) return;
     if (na < m_limit) m_limit = na;
   } else {
     const int live_k = (int)ceil_div(na * (int64_t)sizeof(T), kStageBytes);
     if (live_k < nk) nk = live_k;
   }
   int tm, tn;
-  tile_coords(blockIdx.x, nwg, tiles_m, tiles_n, a.group_m, tm, tn);
+  tile_coords(bid, nwg, tiles_m, tiles_n, a.group_m, tm, tn);
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
   f32x4 acc[kBI][kBJ];
   zero_acc(acc);
@@ -357,6 +359,25 @@ __global__ __launch_bounds__(kThreads) void product_kernel(ProductArgs a, int ti
       }
     }
   }
+}
+
+// dH and dW in one launch.  Workgroups [0, dh_slots) take dH tiles (long: K runs
+// over the vocabulary), the rest dW tiles (short: K runs over the live rows).  The
+// dH tiles are dispatched first, and the dW tiles fill the CUs that the last
+// partial round of dH tiles leaves idle.  dh_slots is a multiple of 8, so a dW
+// workgroup's XCD is still its index modulo 8.
+template <typename T, typename O>
+__global__ __launch_bounds__(kThreads) void grad_products_kernel(ProductArgs dh, ProductArgs dw,
+                                                                 int dh_slots, int dh_tiles_m,
+                                                                 int dh_tiles_n, int dw_tiles_m,
+                                                                 int dw_tiles_n) {
+  __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+  const int bid = (int)blockIdx.x;
+  if (bid < dh_slots)
+    product_tile<T, 0, O>(dh, bid, dh_tiles_m * dh_tiles_n, dh_tiles_m, dh_tiles_n, lds);
+  else
+    product_tile<T, 1, O>(dw, bid - dh_slots, (int)gridDim.x - dh_slots, dw_tiles_m, dw_tiles_n,
+                          lds);
 }
 
 // The chunk's live H rows, Hg[r][d] = H[rows[r]][d] and HT[d][r] (HT rows are
@@ -488,10 +509,6 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     ProductArgs ph{nt_vtiled(dz, R, esz, (int64_t)tiles_v * R * 256 * esz),
                    mn_row_major(a.W, D * esz, a.v_real, D, esz), (int)(VK * esz / kStageBytes),
                    dH + c0 * D, D, nc, D, INT64_MAX, 0, a.group_dh, live, rows};
-    hipLaunchKernelGGL((product_kernel<T, 0, O>), dim3(tiles_t * tiles_d), dim3(kThreads), 0, s,
-                       ph, tiles_t, tiles_d);
-    ev.mark(8, s);
-    ev.mark(9, s);
 
     // dW: M = d (HT K-contiguous), N = v (dz read MN-contiguous), K = live row.
     // Rows [v_real, VK) of the last tile are written as zeros, or, when
@@ -500,9 +517,10 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
                    (int)(ncp * esz / kStageBytes), dW, D, D,
                    a.accumulate_dw ? a.v_real : (a.v_rows < VK ? a.v_rows : VK), a.v_real,
                    (c0 > 0 || a.accumulate_dw) ? 1 : 0, a.group_dw, live, nullptr};
-    hipLaunchKernelGGL((product_kernel<T, 1, O>), dim3(tiles_d * tiles_v), dim3(kThreads), 0, s,
-                       pw, tiles_d, tiles_v);
-    ev.mark(10, s);
+    const int dh_slots = (int)ceil_div((int64_t)tiles_t * tiles_d, 8) * 8;
+    hipLaunchKernelGGL((grad_products_kernel<T, O>), dim3(dh_slots + tiles_d * tiles_v),
+                       dim3(kThreads), 0, s, ph, pw, dh_slots, tiles_t, tiles_d, tiles_d, tiles_v);
+    ev.mark(8, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
