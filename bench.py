@@ -39,6 +39,10 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=3072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--steps-only", action="store_true",
+                    help="time the steps only (no log-prob entry, shard or variant timings): "
+                         "for profiler runs whose per-kernel records should hold step "
+                         "launches alone")
     return ap.parse_args()
 
 
@@ -234,6 +238,21 @@ def main():
     ms_step = start.elapsed_time(end) / K
     value = N / (ms_step / 1e3)
 
+    extra = {} if args.steps_only else extra_timings(args, gb, p, d, head, inp, cfg, dH, dW,
+                                                     stream, torch)
+    stages = {}
+    for name, (a, b) in gb.STAGES.items():
+        stages[name] = float(np.mean([hev.elapsed_ms(evs[k][a], evs[k][b]) for k in range(K)]))
+    per_step = [hev.elapsed_ms(evs[k][0], evs[k][gb.N_STAGE_EVENTS - 1]) for k in range(K)]
+    hev.destroy()
+    report(args, cfg, inp, N, D, V, n_live, K, ms_step, value, wall, stages, per_step, extra)
+
+
+def extra_timings(args, gb, p, d, head, inp, cfg, dH, dW, stream, torch):
+    """The entry points and variants timed after the steps, on the same inputs."""
+    N, D, V = cfg.n_tokens, cfg.d_model, cfg.v_real
+    dev = d["H"].device
+    K = args.steps
     # the forward-only selected log-prob entry (how a trainer gets the old and the
     # reference policy's log-probs) on the same inputs, timed after the steps
     lp_ws = torch.empty(gb.logp_workspace_size(p), dtype=torch.uint8, device=dev)
@@ -302,12 +321,20 @@ def main():
 
     ms_b16 = variant_ms(p_b16, dH16, dW16)
     ms_acc = variant_ms(p_acc, dH, dW)
+    return {
+        "logp_entry": {"ms": round(ms_logp, 3), "calls": K2,
+                       "tokens_per_s": round(N / (ms_logp / 1e3), 1),
+                       "tflops_2nvd": round(2.0 * N * V * D / (ms_logp / 1e3) / 1e12, 1)},
+        "variant_steps_ms": {"bf16_grads": round(ms_b16, 3), "accumulate_dw": round(ms_acc, 3),
+                             "steps": K2},
+        "tp2_shard_tiles": {"v_rows": v_half, "ms": round(ms_shard, 3),
+                            "tflops": round(2.0 * N * v_half * D / (ms_shard / 1e3) / 1e12, 1)},
+    }
 
-    stages = {}
-    for name, (a, b) in gb.STAGES.items():
-        stages[name] = float(np.mean([hev.elapsed_ms(evs[k][a], evs[k][b]) for k in range(K)]))
-    per_step = [hev.elapsed_ms(evs[k][0], evs[k][gb.N_STAGE_EVENTS - 1]) for k in range(K)]
-    hev.destroy()
+
+def report(args, cfg, inp, N, D, V, n_live, K, ms_step, value, wall, stages, per_step, extra):
+    """Print the JSON line."""
+    from lm_head_selected_amd import binding as gb
 
     # algorithmic flops of each matrix-core launch: 2 D V (real vocabulary rows) per
     # row it processes: every token in the forward, the live rows in the backward
@@ -347,14 +374,8 @@ def main():
         "stages_ms": {k: round(v, 3) for k, v in stages.items()},
         "wall_s": round(wall, 3),
         "roofline": roofline,
-        "logp_entry": {"ms": round(ms_logp, 3), "calls": K2,
-                       "tokens_per_s": round(N / (ms_logp / 1e3), 1),
-                       "tflops_2nvd": round(2.0 * N * V * D / (ms_logp / 1e3) / 1e12, 1)},
-        "variant_steps_ms": {"bf16_grads": round(ms_b16, 3), "accumulate_dw": round(ms_acc, 3),
-                             "steps": K2},
-        "tp2_shard_tiles": {"v_rows": v_half, "ms": round(ms_shard, 3),
-                            "tflops": round(2.0 * N * v_half * D / (ms_shard / 1e3) / 1e12, 1)},
     }
+    out.update(extra)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
     print(json.dumps(out), flush=True)

@@ -490,7 +490,7 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(zero_dead_rows_kernel<O>, dim3((unsigned)ceil_div(nc, 4)), dim3(256), 0, s,
                        (const int32_t*)rowpos, nc, D, dH + c0 * D);
 
-    DlogitsArgs d{a.W, hg, gl, nc, D, a.v_real, a.inv_tau, dz, R, a.group_fwd, live};
+    DlogitsArgs d{a.W, hg, gl, nc, D, a.v_real, a.inv_tau, dz, R, a.group_dlogits, live};
     ev.mark(5, s);
     hipLaunchKernelGGL(dlogits_kernel<T>, dim3(tiles_v * tiles_t), dim3(kThreads), 0, s, d,
                        tiles_v, tiles_t);

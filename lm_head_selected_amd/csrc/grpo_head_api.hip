@@ -148,13 +148,17 @@ gh::WsLayout layout(const grpo_head_params* p, bool with_gemm = true) {
 }
 
 // Tile-order group sizes (M-tiles walked per N-tile), chosen by measurement.
-constexpr int kGroupDh = 4, kGroupDw = 4;
+// dH and dW: 4 (8 and 2 measured slower).  The backward's logit recompute
+// (dlogits): 4, also where the forward takes 8 -- it streams 128 KB of dz out
+// per tile besides its operands; on the Qwen3-8B head at 8192 tokens 4 ran 3-4%
+// faster than 8, and 2, 3 and 6 in between.
+constexpr int kGroupDh = 4, kGroupDw = 4, kGroupDlogits = 4;
 
-// Group size of the two logit products (vocabulary tiles walked per token tile).
-// The W panels of the groups resident on the 8 XCDs, plus all of H, should fit in
-// the 256 MB last-level cache; otherwise both are fetched from HBM again and
-// again.  Measured on the Qwen3-8B head: 8 is best at 8192 tokens and 4 at 16384
-// (which runs 7% slower with 8); 16 is slower at both, 2 slower at 16384.
+// Group size of the forward's logit product (vocabulary tiles walked per token
+// tile).  The W panels of the groups resident on the 8 XCDs, plus all of H, should
+// fit in the 256 MB last-level cache; otherwise both are fetched from HBM again
+// and again.  Measured on the Qwen3-8B head: 8 is best at 8192 tokens and 4 at
+// 16384 (which runs 7% slower with 8); 16 is slower at both, 2 slower at 16384.
 int logit_group(int64_t tokens, int64_t d_model, int64_t esz) {
   const int64_t budget = (int64_t)192 << 20;
   const int64_t panel = 256 * d_model * esz, h = tokens * d_model * esz;
@@ -451,9 +455,7 @@ int grpo_head_bwd(const grpo_head_params* p, const void* H, const void* W, const
   g_marks.mark(4, s);
   gh::BwdArgs ba{H, W, y, mask, lse, coef, grad_output, dH, dW, p->n_tokens, p->d_model,
                  p->v_real, p->v_rows, p->ignore_index, p->inv_tau, w, &L,
-                 logit_group(L.chunk < p->n_tokens ? L.chunk : p->n_tokens, p->d_model,
-                             p->dtype == GRPO_HEAD_F32 ? 4 : 2),
-                 kGroupDh, kGroupDw, &g_marks, p->accumulate_dw,
+                 kGroupDlogits, kGroupDh, kGroupDw, &g_marks, p->accumulate_dw,
                  p->grad_dtype == GRPO_HEAD_GRAD_BF16 ? 1 : 0};
   hipError_t e = gh::launch_bwd(p->dtype, ba, s);
   if (e != hipSuccess) return hip_fail(e, "backward kernels");

@@ -96,7 +96,7 @@ struct BwdArgs {
   int64_t n_tokens, d_model, v_real, v_rows, ignore_index;
   float inv_tau;
   char* ws; const WsLayout* L;
-  int group_fwd, group_dh, group_dw;
+  int group_dlogits, group_dh, group_dw;
   const StageEvents* marks;
   int accumulate_dw;   // add the gradient to dW rows [0, v_real) instead of overwriting
   int grad_bf16;       // dH and dW are bf16 (else fp32)
