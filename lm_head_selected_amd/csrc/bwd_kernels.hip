@@ -149,20 +149,22 @@ __global__ __launch_bounds__(kCompactBlock) void compact_kernel(CompactArgs a) {
   }
 }
 
-// dz[t][v] = -g_t p_tv over the tile (the target element is rewritten afterwards
-// by the target-logit kernel).  Columns of padded vocabulary rows hold finite
-// values that the products never use: they meet zero rows of W in dH, and the
-// padded rows of dW are written as zeros.  Token rows past the chunk get g = 0.
+// dz[r][v] = -g_r p_rv over the tile, for live row r (the target element is
+// rewritten afterwards by the target-logit kernel).  Columns of padded vocabulary
+// rows hold finite values that the products never use: they meet zero rows of W in
+// dH, and the padded rows of dW are written as zeros.  Rows past the live count get
+// g = 0 and zero H rows, so their dz is zero.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int tiles_m,
                                                            int tiles_n) {
   __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
   // the launch covers every token tile of the chunk; only those holding live rows run
   const int live_n = (int)ceil_div((int64_t)*a.live, kTile);
-  const int nwg = tiles_m * (live_n < tiles_n ? live_n : tiles_n);
+  if (live_n < tiles_n) tiles_n = live_n;
+  const int nwg = tiles_m * tiles_n;
   if ((int)blockIdx.x >= nwg) return;
   int tm, tn;
-  tile_coords(blockIdx.x, nwg, tiles_m, live_n < tiles_n ? live_n : tiles_n, a.group_m, tm, tn);
+  tile_coords(blockIdx.x, nwg, tiles_m, tiles_n, a.group_m, tm, tn);
   const int64_t v0 = (int64_t)tm * kTile, t0 = (int64_t)tn * kTile;
   const int64_t esz = Elem<T>::size;
   const Operand A = nt_row_major(a.W, a.d_model * esz, a.v_real);
@@ -225,7 +227,8 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
 }
 
 // Products with a K-contiguous A and an MN-contiguous B.
-//   kRole 0 (dH): C[m = t][n = d] stored row-major: out[m * ld_out + n];
+//   kRole 0 (dH): C[m = live row r][n = d] stored row-major at the row's token:
+//                 out[out_rows[m] * ld_out + n];
 //   kRole 1 (dW): C[m = d][n = v] stored as out[n * ld_out + m .. + 3].
 struct ProductArgs {
   Operand A, B;
