@@ -35,7 +35,7 @@ STAGES = {"fwd_tiles": (0, 1), "fwd_tail": (1, 2), "fwd_objective": (2, 3),
           "bwd_prep": (4, 5), "bwd_dlogits": (5, 6), "bwd_target": (6, 7),
           "bwd_grads": (7, 8)}
 # stages that are exactly one matrix-core launch, with that launch's kernel symbol stem
-GEMM_STAGES = {"fwd_tiles": "fwd_tile_kernel", "bwd_dlogits": "dlogits_kernel",
+GEMM_STAGES = {"fwd_tiles": "fwd_tile_chain_kernel", "bwd_dlogits": "dlogits_kernel",
                "bwd_grads": "grad_products_kernel<__bf16, float>"}
 
 

@@ -25,37 +25,20 @@ __device__ __forceinline__ bool token_active(const uint8_t* mask, const int64_t*
   return mask ? (mask[t] != 0) : (y[t] != ignore_index);
 }
 
-// The tile holding the vocabulary's ragged end masks its rows >= v_real (padding:
-// their W rows load as zeros) to -inf; the branch is uniform per workgroup.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int tiles_m,
-                                                            int tiles_n) {
-  // One LDS object only: with a second __shared__ array the compiler can no longer
-  // tell the direct-to-LDS loads from the fragment reads and waits for every load
-  // right after issuing it.  The per-half row statistics reuse the pipeline's
-  // buffers once the K loop has drained.
-  __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
-  static_assert(sizeof(float2) * 2 * kTile <= kGemmLds, "row statistics fit in LDS");
-
-  int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, a.group_m, tm, tn);
-  const int64_t v0 = (int64_t)tm * kTile;   // vocabulary rows of this tile
-  const bool partial = v0 + kTile > a.v_real;
-  const int64_t t0 = (int64_t)tn * kTile;   // tokens of this tile
-  const int64_t esz = Elem<T>::size;
-
-  const Operand A = nt_row_major(a.W, a.d_model * esz, a.v_real);
-  const Operand B = nt_row_major(a.H, a.d_model * esz, a.n_tokens);
-  f32x4 acc[kBI][kBJ];
-  zero_acc(acc);
-  gemm_tile<T, false, false>(A, B, v0, t0, (int)(a.d_model * esz / kStageBytes), (lds_t*)lds,
-                             acc);
-
+// The (max, sumexp) partial of every token column of a finished logit tile
+// (vocabulary rows v0 .. v0 + 255, tokens t0 .. t0 + 255) in base-2 units.  The
+// tile holding the vocabulary's ragged end first masks its rows >= v_real
+// (padding: their W rows loaded as zeros) to -inf; the branch is uniform per
+// workgroup.  half_stats is 4 KB of LDS for the two 128-row halves.  kChained:
+// the next tile's loads are in flight, so the barrier waits on LDS only.
+template <bool kChained>
+__device__ __forceinline__ void tile_partials(f32x4 (&acc)[kBI][kBJ], const FwdTileArgs& a,
+                                              int tm, int64_t v0, int64_t t0,
+                                              float2 (*half_stats)[kTile]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWN, wn = wave % kWN;
   const float c2 = a.inv_tau * kLog2e;
-  float2(*half_stats)[kTile] = (float2(*)[kTile])lds;   // [2][kTile]
-  if (partial) {
+  if (v0 + kTile > a.v_real) {
     const int64_t left = a.v_real - (v0 + wm * 128);
     mask_rows(acc, (int)(left < 0 ? 0 : (left > 128 ? 128 : left)));
   }
@@ -86,7 +69,8 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int t
     // all four lane groups hold the same (m, s); all write it
     half_stats[wm][tl] = make_float2(m, s);
   }
-  __syncthreads();
+  if (kChained) pipe_barrier();
+  else __syncthreads();
 
   // merge the two 128-row halves (wave rows 0 then 1) and write the tile partial
   const int tl = threadIdx.x;
@@ -101,6 +85,76 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int t
       S = p0.y * fast_exp2(p0.x - M) + p1.y * fast_exp2(p1.x - M);
     }
     a.partials[(int64_t)tm * a.n_tokens + t] = make_float2(M, S);
+  }
+}
+
+// One workgroup per logit tile.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int tiles_m,
+                                                            int tiles_n) {
+  // One LDS object only: with a second __shared__ array the compiler can no longer
+  // tell the direct-to-LDS loads from the fragment reads and waits for every load
+  // right after issuing it.  The per-half row statistics reuse the pipeline's
+  // buffers once the K loop has drained.
+  __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+  static_assert(sizeof(float2) * 2 * kTile <= kGemmLds, "row statistics fit in LDS");
+
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, a.group_m, tm, tn);
+  const int64_t v0 = (int64_t)tm * kTile;   // vocabulary rows of this tile
+  const int64_t t0 = (int64_t)tn * kTile;   // tokens of this tile
+  const int64_t esz = Elem<T>::size;
+
+  const Operand A = nt_row_major(a.W, a.d_model * esz, a.v_real);
+  const Operand B = nt_row_major(a.H, a.d_model * esz, a.n_tokens);
+  f32x4 acc[kBI][kBJ];
+  zero_acc(acc);
+  gemm_tile<T, false, false>(A, B, v0, t0, (int)(a.d_model * esz / kStageBytes), (lds_t*)lds,
+                             acc);
+  tile_partials<false>(acc, a, tm, v0, t0, (float2(*)[kTile])lds);
+}
+
+// A fixed number of workgroups (a multiple of 8), each computing a sequence of
+// logit tiles with the K pipeline running on from one tile into the next
+// (gemm_tile_chain), so a tile's epilogue overlaps the next tile's first loads.
+// Workgroup b sits on XCD b % 8 and walks that XCD's run of logical tile ids (the
+// runs tile_coords gives the XCDs), strided by the number of workgroups per XCD:
+// the tiles resident together on an XCD are the same as with one workgroup per
+// tile.  Needs an even number of K stages.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void fwd_tile_chain_kernel(FwdTileArgs a, int tiles_m,
+                                                                  int tiles_n) {
+  // pipeline buffers, then the per-half row statistics (one LDS object: see above)
+  __shared__ __attribute__((aligned(16))) char lds[kGemmLds + 2 * kTile * sizeof(float2)];
+  const int total = tiles_m * tiles_n;
+  const int xcd = (int)blockIdx.x & 7, per_xcd = (int)gridDim.x >> 3;
+  const int q = total >> 3, r = total & 7;
+  const int start = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+  const int len = q + (xcd < r ? 1 : 0);
+  int id = (int)blockIdx.x >> 3;
+  if (id >= len) return;
+  const int64_t esz = Elem<T>::size;
+  const int nk = (int)(a.d_model * esz / kStageBytes);
+  const Operand A = nt_row_major(a.W, a.d_model * esz, a.v_real);
+  const Operand B = nt_row_major(a.H, a.d_model * esz, a.n_tokens);
+  float2(*half_stats)[kTile] = (float2(*)[kTile])(lds + kGemmLds);
+  i32x4 fa0[kBI], fb0[kBJ];
+  int tm, tn;
+  logical_coords(start + id, tiles_m, tiles_n, a.group_m, tm, tn);
+  for (bool first = true; id < len; first = false) {
+    const int nid = id + per_xcd;
+    const bool has_next = nid < len;
+    int tmn = tm, tnn = tn;
+    if (has_next) logical_coords(start + nid, tiles_m, tiles_n, a.group_m, tmn, tnn);
+    const int64_t v0 = (int64_t)tm * kTile, t0 = (int64_t)tn * kTile;
+    f32x4 acc[kBI][kBJ];
+    zero_acc(acc);
+    gemm_tile_chain<T>(A, B, v0, t0, has_next, (int64_t)tmn * kTile, (int64_t)tnn * kTile, nk,
+                       first, (lds_t*)lds, acc, fa0, fb0);
+    tile_partials<true>(acc, a, tm, v0, t0, half_stats);
+    id = nid;
+    tm = tmn;
+    tn = tnn;
   }
 }
 
@@ -216,11 +270,35 @@ __global__ __launch_bounds__(kMergeTokens * kMergeRuns) void merge_kernel(MergeA
   a.logp[t] = lp;
 }
 
+// Workgroups of the chained forward: one per compute unit of the current device
+// (a multiple of 8), looked up once per device.
+static int chain_workgroups() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = cus / 8 * 8;
+  }
+  return cached[dev];
+}
+
 template <typename T>
 static void launch_tiles(const FwdTileArgs& a, int tiles_m, int tiles_n,
                          const StageEvents& ev, hipStream_t s) {
-  hipLaunchKernelGGL(fwd_tile_kernel<T>, dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,
-                     tiles_m, tiles_n);
+  const int64_t nk = a.d_model * (int64_t)sizeof(T) / kStageBytes;
+  const int g = chain_workgroups();
+  if (nk % 2 == 0 && g >= 8) {
+    const int total = tiles_m * tiles_n;
+    const int used = total < g ? (total + 7) / 8 * 8 : g;
+    hipLaunchKernelGGL(fwd_tile_chain_kernel<T>, dim3(used), dim3(kThreads), 0, s, a, tiles_m,
+                       tiles_n);
+  } else {
+    hipLaunchKernelGGL(fwd_tile_kernel<T>, dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,
+                       tiles_m, tiles_n);
+  }
   ev.mark(1, s);
 }
 

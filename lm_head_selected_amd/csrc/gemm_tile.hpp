@@ -415,6 +415,115 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   pipe_barrier();
 }
 
+// gemm_tile for two K-contiguous operands, chained across the tiles one workgroup
+// computes in turn (an even number of K stages, so stage s of every tile sits in
+// LDS buffer s % 2).  The loads that gemm_tile spends on the two stages past the
+// end of K fetch the next tile's stages 0 and 1 instead, and the last fragment
+// read of the loop is the next tile's first: on return with has_next, fa0/fb0 hold
+// those fragments and stage 1 is in flight, which is the state gemm_tile's prologue
+// builds.  The caller's epilogue may then use LDS outside the pipeline buffers and
+// wait on LDS only (pipe_barrier), and calls again with first = false.  Without a
+// next tile the loads are drained before returning, as in gemm_tile.
+template <typename T>
+__device__ __forceinline__ void gemm_tile_chain(const Operand& A, const Operand& B, int64_t m0,
+                                                int64_t n0, bool has_next, int64_t m0n,
+                                                int64_t n0n, int nk, bool first, lds_t* lds,
+                                                f32x4 (&acc)[kBI][kBJ], i32x4 (&fa0)[kBI],
+                                                i32x4 (&fb0)[kBJ]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWN, wn = wave % kWN;
+
+  const TileRange ta = tile_range(A, m0), tb = tile_range(B, n0);
+  const TileRange tan = tile_range(A, has_next ? m0n : m0);
+  const TileRange tbn = tile_range(B, has_next ? n0n : n0);
+  const int rA = wm * (kTile / kWM), rB = wn * (kTile / kWN);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  // waves 0-3 issue every load of a stage (as gemm_tile does for two K-contiguous
+  // operands); stages nk and nk + 1 come from the next tile when there is one
+  constexpr int kHalf = kWaves / 2;
+  const int lw = wave & (kHalf - 1);
+  uint32_t stepA, stepB;
+  const uint32_t offA0 = load_offset<T>(A, lw, lane, stepA);
+  const uint32_t offA1 = load_offset<T>(A, lw + kHalf, lane, stepA);
+  const uint32_t offB0 = load_offset<T>(B, lw, lane, stepB);
+  const uint32_t offB1 = load_offset<T>(B, lw + kHalf, lane, stepB);
+  auto issue = [&](int stage) {
+    if (wave >= kHalf) return;
+    const uint32_t s0 = lds_base + (stage & 1) * kStageLds + lw * 1024;
+    const uint32_t s1 = s0 + kHalf * 1024;
+    const bool nxt = has_next && stage >= nk;
+    const int ks = nxt ? stage - nk : stage;
+    const __amdgpu_buffer_rsrc_t ra = stage_rsrc<T>(A, nxt ? tan : ta, ks);
+    const __amdgpu_buffer_rsrc_t rb = stage_rsrc<T>(B, nxt ? tbn : tb, ks);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const uint32_t ia = __builtin_amdgcn_readfirstlane(i * stepA);
+      const uint32_t ib = __builtin_amdgcn_readfirstlane(i * stepB);
+      const uint32_t l0 = __builtin_amdgcn_readfirstlane(s0 + i * kWaves * 1024);
+      const uint32_t l1 = __builtin_amdgcn_readfirstlane(s1 + i * kWaves * 1024);
+      dma16(ra, offA0, ia, l0);
+      dma16(rb, offB0, ib, l0 + kOpLds);
+      dma16(ra, offA1, ia, l1);
+      dma16(rb, offB1, ib, l1 + kOpLds);
+    }
+  };
+  auto quarter = [&](const i32x4 (&ca)[kBI], const i32x4 (&cb)[kBJ], i32x4 (&na)[kBI],
+                     i32x4 (&nb)[kBJ], int rstage, int rks, int c) {
+    const lds_t* s = lds + (rstage & 1) * kStageLds;
+    if (c == 0) {
+#pragma unroll
+      for (int j = 0; j < kBJ; ++j) nb[j] = read_frag<T, false>(s + kOpLds, rB + 16 * j, rks, lane);
+    }
+    na[2 * c] = read_frag<T, false>(s, rA + 16 * (2 * c), rks, lane);
+    na[2 * c + 1] = read_frag<T, false>(s, rA + 16 * (2 * c + 1), rks, lane);
+#pragma unroll
+    for (int i = 2 * c; i < 2 * c + 2; ++i)
+#pragma unroll
+      for (int j = 0; j < kBJ; ++j) Mma<T>::run(acc[i][j], ca[i], cb[j]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  i32x4 fa1[kBI], fb1[kBJ];
+  if (first) {
+    issue(0);
+    issue(1);
+    wait_vm<4 * kLoads>();   // stage 0 landed; stage 1 may be in flight
+    pipe_barrier();
+    const lds_t* s = lds;
+#pragma unroll
+    for (int i = 0; i < kBI; ++i) fa0[i] = read_frag<T, false>(s, rA + 16 * i, 0, lane);
+#pragma unroll
+    for (int j = 0; j < kBJ; ++j) fb0[j] = read_frag<T, false>(s + kOpLds, rB + 16 * j, 0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) quarter(fa0, fb0, fa1, fb1, kt, 1, c);
+    wait_vm<0>();
+    pipe_barrier();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      quarter(fa1, fb1, fa0, fb0, kt + 1, 0, c);
+      if (c == 0) {
+        issue(kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  if (!has_next) {
+    wait_vm<0>();
+    pipe_barrier();
+  }
+}
+
 // Set every accumulator whose wave-local M row (0..127) is >= vlim to -inf.
 // Used once per tile, only on the tile holding the vocabulary's ragged end.
 __device__ __forceinline__ void mask_rows(f32x4 (&acc)[kBI][kBJ], int vlim) {
