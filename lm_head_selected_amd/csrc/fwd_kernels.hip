@@ -126,11 +126,9 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_chain_kernel(FwdTileArgs a,
                                                                   int tiles_n) {
   // pipeline buffers, then the per-half row statistics (one LDS object: see above)
   __shared__ __attribute__((aligned(16))) char lds[kGemmLds + 2 * kTile * sizeof(float2)];
-  const int total = tiles_m * tiles_n;
-  const int xcd = (int)blockIdx.x & 7, per_xcd = (int)gridDim.x >> 3;
-  const int q = total >> 3, r = total & 7;
-  const int start = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
-  const int len = q + (xcd < r ? 1 : 0);
+  const int per_xcd = (int)gridDim.x >> 3;
+  int start, len;
+  xcd_run((int)blockIdx.x & 7, tiles_m * tiles_n, start, len);
   int id = (int)blockIdx.x >> 3;
   if (id >= len) return;
   const int64_t esz = Elem<T>::size;

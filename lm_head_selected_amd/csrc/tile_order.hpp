@@ -17,6 +17,14 @@ GH_HOST_DEVICE inline int xcd_logical(int bid, int nwg) {
   return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
+// The run of logical ids [start, start + len) that xcd_logical gives XCD `xcd` in a
+// launch of `total` workgroups.
+GH_HOST_DEVICE inline void xcd_run(int xcd, int total, int& start, int& len) {
+  const int q = total >> 3, r = total & 7;
+  start = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+  len = q + (xcd < r ? 1 : 0);
+}
+
 // Logical tile id -> (M tile, N tile): ids walk `group_m` M-tiles down one N-tile
 // before moving to the next N-tile, so workgroups resident together on one XCD
 // share operand slices in that XCD's L2.

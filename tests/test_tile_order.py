@@ -1,6 +1,8 @@
 """The matrix-core launches' tile order (csrc/tile_order.hpp) compiled on the host
-with g++: every workgroup-to-tile mapping is a bijection onto the tile grid, and a
-launch of fewer workgroups covers exactly the first logical ids."""
+with g++: every workgroup-to-tile mapping is a bijection onto the tile grid, a
+launch of fewer workgroups covers exactly the first logical ids, and the chained
+forward's walk (a fixed number of workgroups, each taking every (nwg/8)-th id of
+its XCD's run) computes every tile exactly once."""
 import os
 import shutil
 import subprocess
@@ -36,6 +38,36 @@ int main(int argc, char** argv) {
     seen[m * tn_ + n]++;
   }
   for (int i = 0; i < tm_ * tn_; ++i) if (seen[i] != 1) { printf("tile %d seen %d\n", i, seen[i]); return 1; }
+  // each XCD's run is the set of ids xcd_logical gives that XCD's workgroups
+  const int total = tm_ * tn_;
+  for (int x = 0; x < 8; ++x) {
+    int start, len;
+    gh::xcd_run(x, total, start, len);
+    int count = 0;
+    for (int b = x; b < total; b += 8) {
+      const int l = gh::xcd_logical(b, total);
+      if (l < start || l >= start + len) { printf("run mismatch\n"); return 1; }
+      ++count;
+    }
+    if (count != len) { printf("run length mismatch\n"); return 1; }
+  }
+  // the chained walk with 8, 256 and ceil8(total) workgroups
+  const int chains[3] = {8, 256, (total + 7) / 8 * 8};
+  for (int c = 0; c < 3; ++c) {
+    const int g8 = chains[c], per = g8 >> 3;
+    std::vector<int> hit(total, 0);
+    for (int b = 0; b < g8; ++b) {
+      int start, len;
+      gh::xcd_run(b & 7, total, start, len);
+      for (int id = b >> 3; id < len; id += per) {
+        int m, n;
+        gh::logical_coords(start + id, tm_, tn_, g, m, n);
+        if (m < 0 || m >= tm_ || n < 0 || n >= tn_) { printf("chain out of range\n"); return 1; }
+        hit[m * tn_ + n]++;
+      }
+    }
+    for (int i = 0; i < total; ++i) if (hit[i] != 1) { printf("chain tile %d hit %d\n", i, hit[i]); return 1; }
+  }
   printf("ok\n");
   return 0;
 }
