@@ -245,8 +245,18 @@ __global__ __launch_bounds__(kMergeTokens * kMergeRuns) void merge_kernel(MergeA
   const int64_t k0 = g * per, k1 = (k0 + per < a.n_vt) ? k0 + per : a.n_vt;
   float M = -INFINITY, S = 0.0f;
   if (t < a.n_tokens) {
+    // loads in batches of 8 (all in flight together), folded in ascending order
     const float2* p = a.partials + t;
-    for (int64_t k = k0; k < k1; ++k) {
+    constexpr int kBatch = 8;
+    int64_t k = k0;
+    for (; k + kBatch <= k1; k += kBatch) {
+      float2 q[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) q[u] = p[(k + u) * a.n_tokens];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) fold(M, S, q[u].x, q[u].y);
+    }
+    for (; k < k1; ++k) {
       const float2 q = p[k * a.n_tokens];
       fold(M, S, q.x, q.y);
     }
