@@ -385,8 +385,9 @@ __global__ __launch_bounds__(kThreads) void grad_products_kernel(ProductArgs dh,
 
 // The chunk's live H rows, Hg[r][d] = H[rows[r]][d] and HT[d][r] (HT rows are
 // ld_out elements long), zero for rows[r] past the live count.  Only the rows the
-// products read are written: those of token tiles holding live rows.  64 x 64
-// element tiles through LDS.
+// products read are written: those of token tiles holding live rows.  Tiles of
+// 64 rows x 64 elements (d_model is a multiple of 64): 16-byte loads and stores,
+// the transpose through LDS.
 template <typename E>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const E* __restrict__ H,
                                                           int64_t d_model,
@@ -394,24 +395,31 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const E* __restrict__ 
                                                           const int32_t* live, E* __restrict__ Hg,
                                                           E* __restrict__ HT, int64_t ld_out,
                                                           int tiles_d) {
-  __shared__ E tile[64][65];
+  constexpr int kV = 16 / (int)sizeof(E);        // elements per 16-byte vector
+  constexpr int kVecs = 64 / kV;                 // vectors per 64-element row
+  constexpr int kPass = 256 / kVecs;             // rows (or columns) per pass
+  struct Vec { E e[kV]; };
+  __shared__ __attribute__((aligned(16))) E tile[64][64 + kV];   // 16-byte aligned rows
   const int64_t td = blockIdx.x % tiles_d, tr = blockIdx.x / tiles_d;
   const int64_t d0 = td * 64, r0 = tr * 64;
   const int64_t na = *live;
   if (r0 >= ceil_div(na, kTile) * kTile) return;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int k = ty; k < 64; k += 4) {
-    const int64_t r = r0 + k, d = d0 + tx;
-    if (d >= d_model) continue;
+  const int c = threadIdx.x % kVecs, q = threadIdx.x / kVecs;
+  for (int k = q; k < 64; k += kPass) {
+    const int64_t r = r0 + k, d = d0 + c * kV;
     const int64_t src = r < na ? rows[r] : -1;
-    const E v = src >= 0 ? H[src * d_model + d] : E(0);
-    tile[k][tx] = v;
-    Hg[r * d_model + d] = v;
+    i32x4 v = {0, 0, 0, 0};
+    if (src >= 0) v = *(const i32x4*)(H + src * d_model + d);
+    *(i32x4*)(Hg + r * d_model + d) = v;
+    *(i32x4*)&tile[k][c * kV] = v;
   }
   __syncthreads();
-  for (int k = ty; k < 64; k += 4) {
-    const int64_t d = d0 + k, r = r0 + tx;
-    if (d < d_model) HT[d * ld_out + r] = tile[tx][k];
+  // column k of the tile: rows c kV .. c kV + kV - 1 as one vector of HT row d0 + k
+  for (int k = q; k < 64; k += kPass) {
+    Vec out;
+#pragma unroll
+    for (int u = 0; u < kV; ++u) out.e[u] = tile[c * kV + u][k];
+    *(i32x4*)(HT + (d0 + k) * ld_out + r0 + c * kV) = __builtin_bit_cast(i32x4, out);
   }
 }
 
