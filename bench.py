@@ -321,11 +321,33 @@ def extra_timings(args, gb, p, d, head, inp, cfg, dH, dW, stream, torch):
 
     ms_b16 = variant_ms(p_b16, dH16, dW16)
     ms_acc = variant_ms(p_acc, dH, dW)
+
+    # the same step with every token live, so the backward skips no row: the mask set
+    # to all ones and the masked tokens' placeholder targets replaced by 0
+    if d["mask"] is not None:
+        y_all = torch.where(d["mask"] != 0, d["y"], torch.zeros_like(d["y"]))
+        m_all = torch.ones_like(d["mask"])
+
+        def all_live():
+            head.fwd(d["H"], d["W"], y_all, m_all, d["sid"], d["adv"], d["old"], d["ref"],
+                     stream=stream)
+            head.bwd(d["H"], d["W"], y_all, m_all, dH=dH, dW=dW, stream=stream)
+        all_live()
+        torch.cuda.synchronize()
+        l0.record(stream)
+        for _ in range(K2):
+            all_live()
+        l1.record(stream)
+        torch.cuda.synchronize()
+        ms_all = l0.elapsed_time(l1) / K2
+    else:
+        ms_all = None
     return {
         "logp_entry": {"ms": round(ms_logp, 3), "calls": K2,
                        "tokens_per_s": round(N / (ms_logp / 1e3), 1),
                        "tflops_2nvd": round(2.0 * N * V * D / (ms_logp / 1e3) / 1e12, 1)},
         "variant_steps_ms": {"bf16_grads": round(ms_b16, 3), "accumulate_dw": round(ms_acc, 3),
+                             "all_rows_live": None if ms_all is None else round(ms_all, 3),
                              "steps": K2},
         "tp2_shard_tiles": {"v_rows": v_half, "ms": round(ms_shard, 3),
                             "tflops": round(2.0 * N * v_half * D / (ms_shard / 1e3) / 1e12, 1)},
