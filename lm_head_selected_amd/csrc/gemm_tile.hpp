@@ -128,13 +128,19 @@ __device__ __forceinline__ int64_t stage_off(const Operand& op, int s) {
 }
 
 // Buffer resource of one K stage of a tile: based at the stage, so per-lane
-// offsets stay small; bytes past the tile's valid range load as zeros.  (The
-// clamp is written on 32-bit halves so it stays in scalar registers.)
+// offsets stay small; bytes past the tile's valid range load as zeros.  With in_k
+// false (a stage past the end of K: the pipeline's two trailing loads, never used)
+// the range is empty, so the loads return zeros without a memory access.  Only the
+// single-tile path with both operands K-contiguous (the backward's dlogits) uses
+// it: there it measured faster, while in the MN-operand products and the chained
+// forward the extra select measured slower.  (The clamp is written on 32-bit halves
+// so it stays in scalar registers.)
 template <typename T>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(const Operand& op,
-                                                             const TileRange& tr, int s) {
+                                                             const TileRange& tr, int s,
+                                                             bool in_k = true) {
   const int64_t o = stage_off<T>(op, s);
-  const int64_t n = tr.limit - o;
+  const int64_t n = in_k ? tr.limit - o : 0;
   const int32_t hi = (int32_t)(n >> 32);
   const uint32_t lo = (uint32_t)n;
   const uint32_t rec = hi < 0 ? 0u : (hi > 0 ? 0xffffffffu : lo);
@@ -285,8 +291,8 @@ constexpr int kIssueSplit = 2;   // waves 0-3 load all of B, waves 4-7 all of A
 // their use -- read stage s + 1's first fragments and multiply stage s's second.
 // The next fragments' LDS reads always run under the current MFMAs, one read
 // between consecutive MFMAs.  The loop has no data-dependent branches: the stages
-// past the end of K are loaded (zeros or unused bytes inside the operand) and
-// read like the others and never used, so every wait count is a constant.  All
+// past the end of K are loaded (zeros, or unused bytes inside the operand) and read
+// like the others and never used, so every wait count is a constant.  All
 // loads are drained before returning: none may write LDS after the workgroup
 // releases it.
 template <typename T, bool kMNA, bool kMNB,
@@ -323,8 +329,8 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
     const bool first = wave < kHalf;
     if (kSolo) {
       if (!first) return;
-      const __amdgpu_buffer_rsrc_t ra = stage_rsrc<T>(A, ta, stage);
-      const __amdgpu_buffer_rsrc_t rb = stage_rsrc<T>(B, tb, stage);
+      const __amdgpu_buffer_rsrc_t ra = stage_rsrc<T>(A, ta, stage, stage < nk);
+      const __amdgpu_buffer_rsrc_t rb = stage_rsrc<T>(B, tb, stage, stage < nk);
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         const uint32_t ia = __builtin_amdgcn_readfirstlane(i * stepA);
