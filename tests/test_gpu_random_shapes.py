@@ -2,8 +2,10 @@
 reach: token counts from 1 upward, hidden sizes of 64 to 320 (odd and even numbers
 of K stages, so both forward tile kernels run), real vocabularies from 1 row with
 0 to 256 padded rows, token chunks, mask densities up to every token inactive,
-both reductions and both element types.  Each case is checked against the oracle,
-dead tokens' dH rows must be exactly zero, and a repeat must be bitwise equal."""
+both reductions and both element types; and packed GSPO segments of random
+lengths with tight and loose clip bounds, with and without the KL term.  Each case
+is checked against the oracle, dead tokens' dH rows must be exactly zero, and a
+repeat must be bitwise equal."""
 import dataclasses
 
 import numpy as np
@@ -65,6 +67,49 @@ def test_random_shape_parity(gb, case):
         d_model=case["d_model"], v_real=case["v_real"], v_rows=case["v_rows"],
         mask_frac=case["mask_frac"], reduction=case["reduction"], seed=5000 + case["k"])
     print(f"case {case}", flush=True)
+    _check(gb, cfg, case)
+
+
+def _gspo_cases(n=8):
+    rng = np.random.default_rng(20261203)
+    out = []
+    for k in range(n):
+        tight = bool(k % 2)          # tight clip bounds: most segments take the clipped branch
+        beta = 0.05 if k % 4 >= 2 else 0.0
+        v_real = int(rng.integers(1, 1500))
+        out.append(dict(
+            k=200 + k, dtype="f32" if k == 3 else "bf16", n_tokens=int(rng.integers(1, 1800)),
+            d_model=64 * int(rng.integers(1, 6)), v_real=v_real,
+            v_rows=v_real + int(rng.choice([0, 100])),
+            seg_len_range=(1, int(rng.integers(2, 400))),
+            eps=(3e-4, 4e-4) if tight else (0.2, 0.2), beta=beta,
+            mask_frac=float(rng.choice([0.0, 0.1, 0.5])), chunk=int(rng.choice([0, 256]))))
+    return out
+
+
+GSPO_CASES = _gspo_cases()
+
+
+@pytest.mark.parametrize("case", GSPO_CASES, ids=lambda c: (
+    f"{c['dtype']}_n{c['n_tokens']}_d{c['d_model']}_v{c['v_real']}r{c['v_rows']}"
+    f"_seg{c['seg_len_range'][1]}_eps{c['eps'][0]}_b{c['beta']}_m{c['mask_frac']}"
+    f"_c{c['chunk']}"))
+def test_random_gspo_parity(gb, case):
+    """Packed GSPO segments of random lengths, tight and loose clip bounds, with and
+    without the KL term (no KL: clipped segments carry no gradient and drop out of
+    the backward)."""
+    cfg = dataclasses.replace(
+        CONFIGS[4], name=f"random_gspo_{case['k']}", dtype=case["dtype"],
+        n_tokens=case["n_tokens"], d_model=case["d_model"], v_real=case["v_real"],
+        v_rows=case["v_rows"], seg_len_range=case["seg_len_range"], eps_low=case["eps"][0],
+        eps_high=case["eps"][1], beta=case["beta"],
+        ref_noise=0.1 if case["beta"] > 0 else None, mask_frac=case["mask_frac"],
+        seed=6000 + case["k"])
+    print(f"case {case}", flush=True)
+    _check(gb, cfg, case)
+
+
+def _check(gb, cfg, case):
     inp, lp, lse = S.with_oracle_logprobs(make_inputs(cfg))
     act = oracle.active_tokens(inp["y"], inp["mask"], inp["ignore_index"])
     d = S.to_device(inp)
