@@ -15,7 +15,8 @@
 // Per token chunk, in ascending chunk order:
 //   1. live_count_kernel, compact_kernel: the live tokens in ascending order
 //      (rows[r] = token, rowpos[t] = r or -1), their (g_t, lse_t log2 e), the count
-//   2. gather_rows_kernel : the live H rows, as Hg[r][d] and transposed HT[d][r]
+//   2. gather_rows_kernel : the live H rows, as Hg[r][d] and transposed, blocked
+//                           by 64 rows, HT[r / 64][d][r % 64]
 //      zero_dead_rows_kernel: dH rows of the dead tokens = 0
 //   3. dlogits_kernel     : -g_t p_tv tile on the matrix cores -> dz (bf16, nearest
 //                           even, on the bf16 path; fp32 on the fp32 path)
@@ -383,8 +384,9 @@ __global__ __launch_bounds__(kThreads) void grad_products_kernel(ProductArgs dh,
                           lds);
 }
 
-// The chunk's live H rows, Hg[r][d] = H[rows[r]][d] and HT[d][r] (HT rows are
-// ld_out elements long), zero for rows[r] past the live count.  Only the rows the
+// The chunk's live H rows, Hg[r][d] = H[rows[r]][d] and transposed, blocked by 64
+// rows: HT[r / 64][d][r % 64] (the dW operand: one K stage of 256 hidden columns is
+// one contiguous run), zero for rows[r] past the live count.  Only the rows the
 // products read are written: those of token tiles holding live rows.  Tiles of
 // 64 rows x 64 elements (d_model is a multiple of 64): 16-byte loads and stores,
 // the transpose through LDS.
@@ -393,8 +395,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const E* __restrict__ 
                                                           int64_t d_model,
                                                           const int32_t* __restrict__ rows,
                                                           const int32_t* live, E* __restrict__ Hg,
-                                                          E* __restrict__ HT, int64_t ld_out,
-                                                          int tiles_d) {
+                                                          E* __restrict__ HT, int tiles_d) {
   constexpr int kV = 16 / (int)sizeof(E);        // elements per 16-byte vector
   constexpr int kVecs = 64 / kV;                 // vectors per 64-element row
   constexpr int kPass = 256 / kVecs;             // rows (or columns) per pass
@@ -414,12 +415,14 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const E* __restrict__ 
     *(i32x4*)&tile[k][c * kV] = v;
   }
   __syncthreads();
-  // column k of the tile: rows c kV .. c kV + kV - 1 as one vector of HT row d0 + k
+  // column k of the tile: rows c kV .. c kV + kV - 1 as one vector of block row
+  // d0 + k; the tile's 64 x 64 block is one contiguous run of HT
+  E* blk = HT + ((r0 >> 6) * d_model + d0) * 64;
   for (int k = q; k < 64; k += kPass) {
     Vec out;
 #pragma unroll
     for (int u = 0; u < kV; ++u) out.e[u] = tile[c * kV + u][k];
-    *(i32x4*)(HT + (d0 + k) * ld_out + r0 + c * kV) = __builtin_bit_cast(i32x4, out);
+    *(i32x4*)(blk + k * 64 + c * kV) = __builtin_bit_cast(i32x4, out);
   }
 }
 
@@ -497,7 +500,7 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     const int ttd = (int)ceil_div(D, 64);
     hipLaunchKernelGGL(gather_rows_kernel<E>, dim3((unsigned)(ttd * (ncp / 64))), dim3(256), 0, s,
                        (const E*)Hc, D, (const int32_t*)rows, (const int32_t*)live, (E*)hg,
-                       (E*)ht, R, ttd);
+                       (E*)ht, ttd);
     hipLaunchKernelGGL(zero_dead_rows_kernel<O>, dim3((unsigned)ceil_div(nc, 4)), dim3(256), 0, s,
                        (const int32_t*)rowpos, nc, D, dH + c0 * D);
 
@@ -524,7 +527,7 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     // dW: M = d (HT K-contiguous), N = v (dz read MN-contiguous), K = live row.
     // Rows [v_real, VK) of the last tile are written as zeros, or, when
     // accumulating into the caller's dW, not written at all.
-    ProductArgs pw{nt_row_major(ht, R * esz, D), mn_vtiled(dz, R, esz, tiles_v),
+    ProductArgs pw{nt_kblocked(ht, D, esz, R * D * esz), mn_vtiled(dz, R, esz, tiles_v),
                    (int)(ncp * esz / kStageBytes), dW, D, D,
                    a.accumulate_dw ? a.v_real : (a.v_rows < VK ? a.v_rows : VK), a.v_real,
                    (c0 > 0 || a.accumulate_dw) ? 1 : 0, a.group_dw, live, nullptr};
