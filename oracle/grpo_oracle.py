@@ -51,7 +51,7 @@ import numpy as np
 __all__ = [
     "widen", "active_tokens", "logits_rows", "lse_rows", "forward", "tile_partials",
     "tiled_lse", "sequence_counts", "grpo_objective", "gspo_objective", "objective",
-    "dlogits_rows", "backward", "dH_rows", "dW_rows", "group_advantage",
+    "dlogits_rows", "backward", "backward_sketch", "dH_rows", "dW_rows", "group_advantage",
 ]
 
 
@@ -206,6 +206,8 @@ def grpo_objective(logp, old, ref, adv, sid, active, n_seqs: int, eps_low: float
     (the (loss, policy_loss, kl) triple of GRPOLossResult).
     coef_t = d loss / d logp_t: the min takes the unclipped term (gradient -a*r)
     when r*a <= c*a, the constant clipped term (gradient 0) otherwise.
+    coef_unclipped / coef_clipped are coef_t as it would be on each branch of the
+    min; at a ratio on a clip boundary both branches are the derivative of one side.
     """
     sid = np.asarray(sid)
     logp = np.asarray(logp, np.float64)
@@ -227,8 +229,11 @@ def grpo_objective(logp, old, ref, adv, sid, active, n_seqs: int, eps_low: float
     policy_loss = float((w * pol).sum())
     kl = float((w * kl_t).sum())
     coef = np.where(active, w * (dpol + beta * dkl), 0.0)
+    coef_unclipped = np.where(active, w * (-a * r + beta * dkl), 0.0)
+    coef_clipped = np.where(active, w * (beta * dkl), 0.0)
     return dict(loss=policy_loss + beta * kl, policy_loss=policy_loss, kl=kl, coef=coef,
-                counts=L, unclipped=unclipped)
+                counts=L, unclipped=unclipped, log_ratio=logp - old,
+                coef_unclipped=coef_unclipped, coef_clipped=coef_clipped)
 
 
 def gspo_objective(logp, old, ref, adv, sid, active, n_seqs: int, eps_low: float,
@@ -244,7 +249,9 @@ def gspo_objective(logp, old, ref, adv, sid, active, n_seqs: int, eps_low: float
     per-token backward coefficient d loss / d logp_t:
       m_t/(S_live L_s) * (-A_s sigma_s [sigma_s A_s <= c_s A_s]) + beta w_t (1 - e^delta_t).
     seg_mean_logp (the ``new_logprobs`` metric) is the active-token mean of logp per
-    segment, 0 for a segment without active tokens.
+    segment, 0 for a segment without active tokens.  rho is each segment's mean
+    log-ratio; coef_unclipped / coef_clipped are coef_t as it would be with its
+    segment on each branch of the min.
     """
     sid = np.asarray(sid)
     logp = np.asarray(logp, np.float64)
@@ -273,13 +280,18 @@ def gspo_objective(logp, old, ref, adv, sid, active, n_seqs: int, eps_low: float
     if S_live == 0:
         zero = np.zeros(len(logp))
         return dict(loss=0.0, policy_loss=0.0, kl=0.0, coef=zero, counts=L,
-                    seg_mean_logp=np.zeros(n_seqs), sigma=sigma, unclipped=g_s != 0)
+                    seg_mean_logp=np.zeros(n_seqs), sigma=sigma, unclipped=g_s != 0,
+                    rho=rho, coef_unclipped=zero, coef_clipped=zero)
     policy_loss = float(pol_s.sum() / S_live)
     kl = float((w * kl_t).sum())
     coef = np.where(active, g_s[sid] / (S_live * Lsafe[sid]) + beta * w * dkl, 0.0)
+    coef_unclipped = np.where(active, -A[sid] * sigma[sid] / (S_live * Lsafe[sid])
+                              + beta * w * dkl, 0.0)
+    coef_clipped = np.where(active, beta * w * dkl, 0.0)
     return dict(loss=policy_loss + beta * kl, policy_loss=policy_loss, kl=kl, coef=coef,
                 counts=L, seg_mean_logp=np.where(live, lsum / Lsafe, 0.0), sigma=sigma,
-                unclipped=live & (sigma * A <= c * A))
+                unclipped=live & (sigma * A <= c * A), rho=rho,
+                coef_unclipped=coef_unclipped, coef_clipped=coef_clipped)
 
 
 def objective(inp: dict, logp) -> dict:
@@ -363,6 +375,31 @@ def backward(H, W, y, active, lse, coef, v_real: int, inv_tau: float, grad_outpu
         dH[r] = G @ W64
         dW[:v_real] += G.T @ H64
     return dH, dW
+
+
+def backward_sketch(H, W, y, active, lse, coef, U, v_real: int, inv_tau: float,
+                    grad_output: float, dtype: str, block: int = 256):
+    """(dH . U, dW . U) for a [D, k] matrix U, without forming dH or dW.
+
+    The same G as ``backward``; by associativity dH U = G (W[:V] U) and
+    dW[:V] U = G^T (H U), and the padded rows of dW U are zero.  A few random
+    columns U summarise every row of both gradients (a sketch), so a full-size
+    gradient can be checked row by row, tile by tile, from [N, k] and [V_r, k]
+    numbers.  Costs one logit pass."""
+    N, D = H.shape
+    U = np.asarray(U, np.float64)
+    W64 = widen(W[:v_real], dtype)
+    WU = W64 @ U
+    sH = np.zeros((N, U.shape[1]))
+    sW = np.zeros((W.shape[0], U.shape[1]))
+    for s in range(0, N, block):
+        r = np.arange(s, min(N, s + block))
+        H64 = widen(H[r], dtype)
+        z = logits_rows(H64, W64, v_real, inv_tau)
+        G = dlogits_rows(z, lse[r], y[r], active[r], coef[r], inv_tau, grad_output)
+        sH[r] = G @ WU
+        sW[:v_real] += G.T @ (H64 @ U)
+    return sH, sW
 
 
 def dH_rows(H, W, y, active, lse, coef, rows, v_real: int, inv_tau: float,

@@ -135,3 +135,36 @@ def test_sampled_rows_equal_full_backward():
     np.testing.assert_allclose(
         oracle.dW_rows(s["H"], s["W"], s["y"], s["act"], s["lse"], coef, vrows, V, INV_TAU, 0.9,
                        "f64", tblock=5), dW[vrows], rtol=1e-12, atol=1e-15)
+
+
+def test_sketch_equals_full_backward_times_probes():
+    """backward_sketch returns (dH U, dW U) of the full backward for a [D, k] U:
+    the same numbers (to rounding) as multiplying the full gradients, with zero
+    rows for inactive tokens and for the padded vocabulary, on bf16 and fp64
+    operands and in blocks that do not divide the token count."""
+    s = _setup(5)
+    coef = s["out"]["coef"]
+    g = np.random.default_rng(9)
+    U = g.standard_normal((D, 3))
+    dH, dW = oracle.backward(s["H"], s["W"], s["y"], s["act"], s["lse"], coef, V, INV_TAU, 1.7,
+                             "f64")
+    sH, sW = oracle.backward_sketch(s["H"], s["W"], s["y"], s["act"], s["lse"], coef, U, V,
+                                    INV_TAU, 1.7, "f64", block=5)
+    np.testing.assert_allclose(sH, dH @ U, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(sW[:V], dW[:V] @ U, rtol=1e-11, atol=1e-14)
+    assert np.all(sW[V:] == 0.0) and np.all(sH[~s["act"]] == 0.0)
+    # a single wrong vocabulary row of dW changes that row of the sketch only
+    dW_bad = dW.copy()
+    dW_bad[7] *= 1.01
+    diff = np.abs(dW_bad[:V] @ U - sW[:V]).max(axis=1)
+    assert np.argmax(diff) == 7 and np.sort(diff)[-2] < 1e-10 * np.abs(sW).max()
+
+    from synth import f32_to_bf16_bits
+    Hb = f32_to_bf16_bits(s["H"].astype(np.float32))
+    Wb = f32_to_bf16_bits(s["W"].astype(np.float32))
+    lp, lse = oracle.forward(Hb, Wb, s["y"], s["act"], V, INV_TAU, "bf16")
+    dH, dW = oracle.backward(Hb, Wb, s["y"], s["act"], lse, coef, V, INV_TAU, 1.0, "bf16")
+    sH, sW = oracle.backward_sketch(Hb, Wb, s["y"], s["act"], lse, coef, U, V, INV_TAU, 1.0,
+                                    "bf16", block=4)
+    np.testing.assert_allclose(sH, dH @ U, rtol=1e-11, atol=1e-14)
+    np.testing.assert_allclose(sW, dW @ U, rtol=1e-11, atol=1e-14)

@@ -233,3 +233,131 @@ def test_fixed_constant_empty_batch_and_bad_constant():
     assert np.all(out["coef"] == 0)
     with pytest.raises(ValueError):
         oracle.grpo_objective(logp, logp, logp, adv, sid, act, 2, .2, .2, .1, "fixed_constant")
+
+
+def test_gspo_kl_weights_closed_form():
+    """GSPO with beta > 0 on segments of unequal length, worked by hand.
+
+    Segment 0: 1 active token; segment 1: 4 tokens, one masked, so L = 3; a third
+    segment is fully masked and drops out of S_live (= 2).  old = logp, so every
+    segment ratio is 1 (unclipped, pol_s = -A_s); ref - logp = delta_s is constant
+    per segment: delta = (0.5, -0.2).
+      k3(0.5)  = e^0.5 - 1.5          = 0.148721270700128
+      k3(-0.2) = e^-0.2 + 0.2 - 1     = 0.018730753077982
+    The KL term weighs each live segment equally (sequence mean):
+      kl = (k3(0.5) + k3(-0.2)) / 2   = 0.083726011889055,
+    whereas a token mean would give (k3(0.5) + 3 k3(-0.2)) / 4 = 0.051228.
+    policy_loss = (-0.7 + 1.3) / 2 = 0.3; loss = 0.3 + 0.1 * kl.
+    coef_t = (-A_s) / (S_live L_s) + beta (1 - e^delta_s) / (S_live L_s):
+      segment 0: -0.7/2 + 0.1 (1 - e^0.5)/2      = -0.382436063535006
+      segment 1:  1.3/6 + 0.1 (1 - e^-0.2)/6     =  0.219687820782017
+    """
+    sid = np.array([0, 1, 1, 1, 1, 2, 2])
+    act = np.array([1, 1, 0, 1, 1, 0, 0], bool)
+    logp = np.array([-0.3, -1.0, -2.0, -0.4, -2.5, -1.0, -1.0])
+    delta = np.array([0.5, -0.2, 0.0])[sid]
+    adv = np.array([0.7, -1.3, 2.0], np.float32)
+    out = oracle.gspo_objective(logp, logp, logp + delta, adv, sid, act, 3, 0.2, 0.28, 0.1)
+    assert out["kl"] == pytest.approx(0.083726011889055, rel=1e-13)
+    assert out["policy_loss"] == pytest.approx(0.3, rel=1e-7)   # adv is fp32: 0.7, -1.3
+    a = adv.astype(np.float64)
+    assert out["policy_loss"] == pytest.approx(-(a[0] + a[1]) / 2.0, rel=1e-14)
+    assert out["loss"] == pytest.approx(out["policy_loss"] + 0.1 * 0.083726011889055, rel=1e-13)
+    c0 = -a[0] / 2 + 0.1 * (1 - np.exp(0.5)) / 2
+    c1 = -a[1] / 6 + 0.1 * (1 - np.exp(-0.2)) / 6
+    assert c0 == pytest.approx(-0.382436063535006, rel=1e-7)
+    assert c1 == pytest.approx(0.219687820782017, rel=1e-7)
+    np.testing.assert_allclose(out["coef"], [c0, c1, 0, c1, c1, 0, 0], rtol=1e-13, atol=0)
+    assert list(out["counts"]) == [1, 3, 0]
+
+
+def test_objective_dispatch_matches_direct_calls():
+    """objective() passes the workload's level, clip bounds, beta, reduction and
+    fixed_constant divisor through unchanged: equal to calling grpo_objective /
+    gspo_objective directly, for distinct eps_low / eps_high, every reduction and
+    both levels, with an explicit mask and in ignore_index mode."""
+    g = np.random.default_rng(21)
+    lens = [5, 3, 6, 2]
+    sid = np.repeat(np.arange(4), lens)
+    n = len(sid)
+    y = g.integers(0, 50, n)
+    mask = (g.random(n) > 0.2).astype(np.uint8)
+    logp = -g.random(n) * 3
+    base = dict(y=y, sid=sid, n_seqs=4, adv=g.standard_normal(4).astype(np.float32),
+                # log-ratios near 0.25 (ratio 1.28): inside 1 + 0.31, outside 1 + 0.13,
+                # so swapped clip bounds would change the result at both levels
+                old_logp=(logp - 0.25 + g.standard_normal(n) * 0.05).astype(np.float32),
+                ref_logp=(logp + g.standard_normal(n) * 0.2).astype(np.float32),
+                eps_low=0.13, eps_high=0.31, beta=0.07, ignore_index=-100)
+    y_ign = y.copy()
+    y_ign[mask == 0] = -100
+    for m, yy in ((mask, y), (None, y_ign)):
+        act = oracle.active_tokens(yy, m, -100)
+        for level, red, C in (("token", "token_mean", None), ("token", "sequence_mean", None),
+                              ("token", "fixed_constant", 23.5),
+                              ("sequence_gspo", "sequence_mean", None)):
+            inp = dict(base, y=yy, mask=m, level=level, reduction=red)
+            if C is not None:
+                inp["norm_const"] = C
+            got = oracle.objective(inp, logp)
+            if level == "token":
+                exp = oracle.grpo_objective(logp, base["old_logp"], base["ref_logp"], base["adv"],
+                                            sid, act, 4, 0.13, 0.31, 0.07, red, C)
+            else:
+                exp = oracle.gspo_objective(logp, base["old_logp"], base["ref_logp"], base["adv"],
+                                            sid, act, 4, 0.13, 0.31, 0.07)
+            for k in ("loss", "policy_loss", "kl"):
+                assert got[k] == exp[k], (level, red, k)
+            np.testing.assert_array_equal(got["coef"], exp["coef"])
+            np.testing.assert_array_equal(got["counts"], exp["counts"])
+    # the two levels and the normalisers really differ on these inputs
+    a = oracle.objective(dict(base, mask=mask, level="token", reduction="token_mean"), logp)
+    b = oracle.objective(dict(base, mask=mask, level="token", reduction="sequence_mean"), logp)
+    c = oracle.objective(dict(base, mask=mask, level="sequence_gspo",
+                              reduction="sequence_mean"), logp)
+    d = oracle.objective(dict(base, mask=mask, level="token", reduction="fixed_constant",
+                              norm_const=23.5), logp)
+    vals = [a["loss"], b["loss"], c["loss"], d["loss"]]
+    assert len({round(v, 12) for v in vals}) == 4
+
+
+@pytest.mark.parametrize("level", ["token", "sequence_gspo"])
+def test_branch_coefficients_are_the_coef_on_either_side_of_a_kink(level):
+    """coef_unclipped / coef_clipped are what coef becomes when a token's (or a
+    segment's) ratio crosses the clip boundary: moving old_logp by 1e-9 across the
+    kink makes the objective take the other branch, and its coef there equals the
+    reported branch coefficient (within the 1e-9 shift)."""
+    eps_l, eps_h, beta = 0.2, 0.28, 0.05
+    lens = [3, 2]
+    sid = np.repeat(np.arange(2), lens)
+    n = len(sid)
+    act = np.ones(n, bool)
+    logp = np.array([-1.0, -2.0, -0.5, -1.5, -0.7])
+    ref = logp + np.array([0.1, -0.2, 0.3, 0.05, -0.1])
+    adv = np.array([1.5, -0.8], np.float32)
+    k_hi, k_lo = np.log1p(eps_h), np.log1p(-eps_l)
+
+    def run(old):
+        if level == "token":
+            return oracle.grpo_objective(logp, old, ref, adv, sid, act, 2, eps_l, eps_h, beta,
+                                         "sequence_mean")
+        return oracle.gspo_objective(logp, old, ref, adv, sid, act, 2, eps_l, eps_h, beta)
+
+    # segment / token log-ratios placed 1e-9 past the boundary the advantage
+    # favours: seq 0 (A > 0) just above 1 + eps_h (clipped), seq 1 (A < 0) just
+    # below 1 - eps_l (clipped)
+    for side in (+1.0, -1.0):
+        lr = np.where(sid == 0, k_hi + side * 1e-9, k_lo - side * 1e-9)
+        old = logp - lr
+        here = run(old)
+        there = run(logp - (lr - side * 2e-9 * np.where(sid == 0, 1.0, -1.0)))
+        flip = here["unclipped"] != there["unclipped"]
+        assert flip.all()
+        for t in range(n):
+            on = "coef_unclipped" if there["unclipped"][t if level == "token" else sid[t]] \
+                else "coef_clipped"
+            assert here[on][t] == pytest.approx(there["coef"][t], rel=1e-7, abs=1e-12)
+            np.testing.assert_array_equal(
+                here["coef"], np.where(
+                    here["unclipped"] if level == "token" else here["unclipped"][sid],
+                    here["coef_unclipped"], here["coef_clipped"]))
