@@ -6,8 +6,12 @@
  * real vocabulary [0, V).  The forward returns each token's selected log-prob
  * log p(y_t) = z[t, y_t] - LSE_v z[t, :] without ever storing the [N, V] logits:
  * vocabulary tiles are streamed, each tile leaves a per-token (max, sumexp)
- * partial, and the partials are folded in ascending tile order from the identity
- * (-inf, 0).  It then applies the clipped-ratio objective and reduces it to
+ * partial, and the partials are folded from the identity (-inf, 0) in one fixed
+ * order: the tiles split into 8 consecutive runs, each run folded in ascending tile
+ * order, then the 8 run results folded in ascending run order (the same order for
+ * every call and every shard count, so results are bitwise repeatable; it differs
+ * from one left-to-right fold only in fp32 rounding).  It then applies the
+ * clipped-ratio objective and reduces it to
  * (loss, policy_loss, kl), and writes the per-token coefficient d loss / d logp_t.
  * The backward recomputes each logit tile, forms
  * dlogits = grad_output * coef_t * (onehot(y_t) - softmax) / tau, and contracts it
@@ -222,7 +226,9 @@ int grpo_head_bwd(const grpo_head_params* p, const void* H, const void* W, const
  *   seg_mean_logp[s] (may be NULL) = mean active-token logp of segment s, 0 if
  *   L_s = 0 (the new_logprobs metric).
  * p->n_tokens, n_seqs, eps_*, beta, ignore_index and validate are used (the GEMM
- * fields d_model, v_real, v_rows, dtype, inv_tau, reduction and level are ignored);
+ * fields d_model, v_real, v_rows, dtype and inv_tau are ignored, and level is
+ * taken as GSPO; the segment mean is the only normaliser, so a reduction of
+ * fixed_constant is rejected with status 1, the other reductions are ignored);
  * y is read only when mask is NULL (then it may not be NULL).  Needs
  * gspo_segment_workspace_size(p) bytes of workspace.
  * Status 0, 1, 2, 6; with validate also 3, 4, 5. */

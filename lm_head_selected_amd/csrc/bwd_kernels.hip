@@ -84,6 +84,8 @@ struct CompactArgs {
   int32_t* rows;      // [n_pad] token of compact row r (-1 past the live rows)
   int32_t* rowpos;    // [n] compact row of token t, -1 if dead
   float2* gl;         // [n_pad] (g_t, lse_t log2 e) of compact row r; (0, 0) past them
+  int32_t* bbase;     // [blocks] live tokens before each block, or null: each block sums
+                      // the counts before it itself (few blocks)
 };
 
 // g_t = grad_output * coef_t / tau for an active token, 0 otherwise.  A token is
@@ -110,6 +112,32 @@ __global__ __launch_bounds__(kCompactBlock) void live_count_kernel(CompactArgs a
   }
 }
 
+// Exclusive prefix sums of the per-block live counts, one block: thread i sums
+// a contiguous run of counts, then the runs' totals are scanned in LDS.  Used when
+// there are many blocks, so compact_kernel's work stays linear in the tokens.
+__global__ __launch_bounds__(kCompactBlock) void block_scan_kernel(const int32_t* bcnt, int nb,
+                                                                   int32_t* bbase) {
+  __shared__ int run[kCompactBlock];
+  const int per = (nb + kCompactBlock - 1) / kCompactBlock;
+  const int b0 = threadIdx.x * per, b1 = b0 + per < nb ? b0 + per : nb;
+  int c = 0;
+  for (int b = b0; b < b1; ++b) c += bcnt[b];
+  run[threadIdx.x] = c;
+  __syncthreads();
+  // Hillis-Steele inclusive scan of the run totals
+  for (int o = 1; o < kCompactBlock; o <<= 1) {
+    const int v = threadIdx.x >= o ? run[threadIdx.x - o] : 0;
+    __syncthreads();
+    run[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int acc = threadIdx.x > 0 ? run[threadIdx.x - 1] : 0;
+  for (int b = b0; b < b1; ++b) {
+    bbase[b] = acc;
+    acc += bcnt[b];
+  }
+}
+
 // Each block places its live tokens after those of the blocks before it, in token
 // order; the last block also writes the count and clears the rows past it.
 __global__ __launch_bounds__(kCompactBlock) void compact_kernel(CompactArgs a) {
@@ -118,9 +146,13 @@ __global__ __launch_bounds__(kCompactBlock) void compact_kernel(CompactArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) {
     int c = 0;
-    for (int b = lane; b < (int)blockIdx.x; b += 64) c += a.bcnt[b];
+    if (a.bbase) {
+      c = a.bbase[blockIdx.x];
+    } else {
+      for (int b = lane; b < (int)blockIdx.x; b += 64) c += a.bcnt[b];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+      for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    }
     if (lane == 0) base = c;
   }
   const int64_t t = (int64_t)blockIdx.x * kCompactBlock + threadIdx.x;
@@ -151,10 +183,13 @@ __global__ __launch_bounds__(kCompactBlock) void compact_kernel(CompactArgs a) {
 }
 
 // dz[r][v] = -g_r p_rv over the tile, for live row r (the target element is
-// rewritten afterwards by the target-logit kernel).  Columns of padded vocabulary
-// rows hold finite values that the products never use: they meet zero rows of W in
-// dH, and the padded rows of dW are written as zeros.  Rows past the live count get
-// g = 0 and zero H rows, so their dz is zero.
+// rewritten afterwards by the target-logit kernel).  On the tile holding the
+// vocabulary's ragged end the padded columns v >= v_real are set to -inf before
+// the exponential, so their dz is zero: their W rows load as zeros, and a zero
+// logit there would otherwise give -g 2^(-lse2), which overflows for a very
+// negative LSE and would turn dH into NaN through 0 * inf.  (The padded rows of dW
+// are written as zeros whatever dz holds.)  Rows past the live count get g = 0 and
+// zero H rows, so their dz is zero.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int tiles_m,
                                                            int tiles_n) {
@@ -177,6 +212,10 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWN, wn = wave % kWN;
+  if (v0 + kTile > a.v_real) {   // uniform per workgroup: only the ragged vocabulary tile
+    const int64_t left = a.v_real - (v0 + wm * (kTile / kWM));
+    mask_rows(acc, (int)(left < 0 ? 0 : (left > 128 ? 128 : left)));
+  }
   const int vl = wm * (kTile / kWM) + (lane >> 4) * 4;   // tile-local vocabulary row
   const float c2 = a.inv_tau * kLog2e;
   // (g, lse2) of the lane's token columns; tokens past the chunk read zeros
@@ -492,10 +531,16 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     const uint8_t* cmask = a.mask ? a.mask + c0 : nullptr;
 
     // live rows of the chunk, their H rows, and zero dH rows for the dead tokens
-    const CompactArgs ca{a.y + c0, cmask, a.ignore_index, a.coef + c0, a.lse + c0, a.grad_output,
-                         a.inv_tau, nc, ncp, bcnt, live, rows, rowpos, gl};
     const unsigned nb = (unsigned)ceil_div(nc, kCompactBlock);
+    // up to 64 blocks each block sums the counts before it in one pass of a wave;
+    // beyond that a scan kernel forms the block offsets first
+    int32_t* bbase = nb > 64 ? bcnt + nb : nullptr;
+    const CompactArgs ca{a.y + c0, cmask, a.ignore_index, a.coef + c0, a.lse + c0, a.grad_output,
+                         a.inv_tau, nc, ncp, bcnt, live, rows, rowpos, gl, bbase};
     hipLaunchKernelGGL(live_count_kernel, dim3(nb), dim3(kCompactBlock), 0, s, ca);
+    if (bbase)
+      hipLaunchKernelGGL(block_scan_kernel, dim3(1), dim3(kCompactBlock), 0, s,
+                         (const int32_t*)bcnt, (int)nb, bbase);
     hipLaunchKernelGGL(compact_kernel, dim3(nb), dim3(kCompactBlock), 0, s, ca);
     const int ttd = (int)ceil_div(D, 64);
     hipLaunchKernelGGL(gather_rows_kernel<E>, dim3((unsigned)(ttd * (ncp / 64))), dim3(256), 0, s,

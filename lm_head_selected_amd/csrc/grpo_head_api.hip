@@ -138,7 +138,7 @@ gh::WsLayout layout(const grpo_head_params* p, bool with_gemm = true) {
   L.gl = take((size_t)chunk * 8);
   L.dz = take((size_t)chunk * L.v_k * esz);   // dlogits of one chunk, v-tiled
   L.ht = take((size_t)D * chunk * esz);       // the chunk's live H rows transposed
-  L.bcnt = take((size_t)gh::ceil_div(chunk, gh::kCompactBlock) * 4);
+  L.bcnt = take((size_t)gh::ceil_div(chunk, gh::kCompactBlock) * 8);   // counts, then offsets
   L.live = take(4);
   L.rows = take((size_t)chunk * 4);
   L.rowpos = take((size_t)chunk * 4);
@@ -277,8 +277,14 @@ size_t grpo_head_workspace_size(const grpo_head_params* p) {
 }
 
 size_t gspo_segment_workspace_size(const grpo_head_params* p) {
-  if (check_common(p, false) != GRPO_HEAD_OK) return 0;
-  return layout(p, false).fwd_bytes;
+  if (!p) {
+    fail(GRPO_HEAD_INVALID_ARGUMENT, "params is NULL");
+    return 0;
+  }
+  grpo_head_params q = *p;
+  q.level = GRPO_HEAD_LEVEL_SEQUENCE_GSPO;
+  if (check_common(&q, false) != GRPO_HEAD_OK) return 0;
+  return layout(&q, false).fwd_bytes;
 }
 
 const char* grpo_head_last_error(void) { return g_last_error.c_str(); }
@@ -475,7 +481,12 @@ int gspo_segment_reduce(const grpo_head_params* p, const float* logp, const floa
                         const int32_t* sid, const float* adv, float* out3, float* coef,
                         float* seg_mean_logp, int32_t* counts, void* ws, size_t ws_bytes,
                         void* stream) {
-  int rc = check_common(p, false);
+  if (!p) return fail(GRPO_HEAD_INVALID_ARGUMENT, "params is NULL");
+  // the segment level is implied: check the block as it will run (GSPO keeps its
+  // segment mean, so a fixed_constant reduction is rejected like in grpo_head_fwd)
+  grpo_head_params q = *p;
+  q.level = GRPO_HEAD_LEVEL_SEQUENCE_GSPO;
+  int rc = check_common(&q, false);
   if (rc) return rc;
   if (!out3) return fail(GRPO_HEAD_INVALID_ARGUMENT, "out3 is NULL");
   if (p->n_seqs > 0 && (!adv || !counts))
@@ -486,8 +497,6 @@ int gspo_segment_reduce(const grpo_head_params* p, const float* logp, const floa
     return fail(GRPO_HEAD_INVALID_ARGUMENT, "y is needed without a mask");
   if (p->beta > 0.0f && p->n_tokens > 0 && !ref_logp)
     return fail(GRPO_HEAD_INVALID_ARGUMENT, "beta > 0 needs ref_logp");
-  grpo_head_params q = *p;
-  q.level = GRPO_HEAD_LEVEL_SEQUENCE_GSPO;
   const gh::WsLayout L = layout(&q, false);
   if (!ws || ws_bytes < L.fwd_bytes)
     return fail(GRPO_HEAD_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, need %zu", ws_bytes,

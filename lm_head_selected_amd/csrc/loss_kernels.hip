@@ -207,11 +207,12 @@ hipError_t launch_loss(const LossArgs& a, hipStream_t s) {
 // the mean subtracted before squaring: RL-Kernel PR #291, review thread on the
 // TWO_PASS enum), divided by G; A = (r - mean) / (std + eps), 0 when that divisor
 // is 0, or A = r - mean without the std scaling.  One thread per group, each sum
-// in index order, so the result is bitwise repeatable.
-__global__ __launch_bounds__(256) void group_advantage_kernel(const float* __restrict__ r,
-                                                              int64_t n_groups, int64_t G,
-                                                              float eps, int scale,
-                                                              float* __restrict__ adv) {
+// in index order, so the result is bitwise repeatable.  adv may be r itself (in
+// place): a thread reads each reward of its group before writing that element,
+// and no other thread touches the group, so r and adv are not restrict.
+__global__ __launch_bounds__(256) void group_advantage_kernel(const float* r, int64_t n_groups,
+                                                              int64_t G, float eps, int scale,
+                                                              float* adv) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= n_groups) return;
   const float* rg = r + g * G;

@@ -183,3 +183,16 @@ def test_shard_bounds():
     q = P(v_real=5000, v_rows=5376)
     assert gb.shard_partials_bytes(q, 5120, 5376) == 0             # padding only: no tiles
     assert gb.lib.grpo_head_merge_partials(ctypes.byref(p), None, 1, 1, None, 1, 1, 0) == 1
+
+
+def test_segment_reduce_rejects_fixed_constant():
+    # GSPO keeps its segment mean: a block asking for the fixed_constant normaliser
+    # is rejected by the standalone seam as by grpo_head_fwd, whatever its level says
+    for level in ("token", "sequence_gspo"):
+        q = P(level=level, reduction="fixed_constant", norm_const=64.0, beta=0.0)
+        assert gb.segment_workspace_size(q) == 0
+        with pytest.raises(gb.GrpoHeadError) as e:
+            gb.gspo_segment_reduce(q, 1, 1, None, 1, None, 1, 1, 1, 1, None, 1, 1,
+                                   ws_bytes=1 << 30, stream=0)
+        assert e.value.status == 1 and "fixed_constant" in str(e.value)
+    assert gb.segment_workspace_size(P(level="token", beta=0.0)) > 0
