@@ -268,6 +268,26 @@ int grpo_head_logp(const grpo_head_params* p, const void* H, const void* W, cons
  * logits).  0 if p is invalid. */
 size_t grpo_head_logp_workspace_size(const grpo_head_params* p);
 
+/* grpo_head_logp without a workspace: for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same outputs, bitwise, as grpo_head_logp; same parameter fields and
+ * statuses.  The scratch grpo_head_logp would take from its workspace lives in a
+ * static device array of GRPO_HEAD_NOALLOC_SCRATCH_BYTES inside the library: each
+ * GPU the library runs on holds one copy until the process ends.  A problem whose
+ * grpo_head_logp_workspace_size(p) exceeds that size is rejected with status 1
+ * before anything is enqueued (64 MiB holds 8192 tokens of a 151936-row vocabulary
+ * with room to spare: about 14100 tokens at that vocabulary).  The call allocates
+ * nothing; its first call on a device looks the array's address up
+ * (hipGetSymbolAddress; a graph-capturing caller can make that first call before
+ * capturing).  Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents: calls that overlap in time on one GPU (other streams or host
+ * threads) race and must be serialised by the caller.  Nothing in the array needs
+ * to start at zero: each call writes every element it later reads. */
+#define GRPO_HEAD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int grpo_head_logp_noalloc(const grpo_head_params* p, const void* H, const void* W,
+                           const int64_t* y, const uint8_t* mask, float* logp, float* lse,
+                           void* stream);
+
 /* One GPU's share of a vocabulary-parallel forward, part 1: the per-tile
  * partials and the target logits of one vocabulary shard, on the global tile
  * grid, so that a fixed-order merge of all shards' partials (part 2) is bitwise

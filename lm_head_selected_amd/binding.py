@@ -27,7 +27,10 @@ EXPORTS = ("grpo_head_fwd_workspace_size", "grpo_head_workspace_size",
            "gspo_segment_workspace_size", "grpo_head_fwd", "grpo_head_bwd",
            "gspo_segment_reduce", "grpo_head_logp", "grpo_head_logp_workspace_size",
            "grpo_group_advantage", "grpo_head_shard_partials", "grpo_head_shard_partials_bytes",
-           "grpo_head_merge_partials", "grpo_head_set_stage_events", "grpo_head_last_error")
+           "grpo_head_merge_partials", "grpo_head_set_stage_events", "grpo_head_last_error",
+           "grpo_head_logp_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # GRPO_HEAD_NOALLOC_SCRATCH_BYTES
 
 # stage-event slots recorded by grpo_head_fwd / grpo_head_bwd
 N_STAGE_EVENTS = 9
@@ -77,6 +80,8 @@ def _load():
     lib.gspo_segment_reduce.restype = i32
     lib.grpo_head_logp.argtypes = [pp] + [vp] * 6 + [vp, sz, vp]
     lib.grpo_head_logp.restype = i32
+    lib.grpo_head_logp_noalloc.argtypes = [pp] + [vp] * 6 + [vp]
+    lib.grpo_head_logp_noalloc.restype = i32
     lib.grpo_group_advantage.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                          ctypes.c_int32, vp, vp]
     lib.grpo_group_advantage.restype = i32
@@ -194,6 +199,11 @@ def grpo_head_logp(p, H, W, y, mask, logp, lse, ws, ws_bytes=None, stream=None):
     ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
     _check(lib.grpo_head_logp(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(y), _ptr(mask), _ptr(logp),
                               _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def grpo_head_logp_noalloc(p, H, W, y, mask, logp, lse, stream=None):
+    _check(lib.grpo_head_logp_noalloc(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(y), _ptr(mask),
+                                      _ptr(logp), _ptr(lse), _stream(stream)))
 
 
 def grpo_group_advantage(rewards, group_size, eps, adv, scale_by_std=True, n_seqs=None,

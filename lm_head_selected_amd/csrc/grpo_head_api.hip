@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/grpo_head.h"
@@ -262,6 +263,38 @@ int check_shard(const grpo_head_params* p, int64_t v_begin, int64_t v_end, int64
   return GRPO_HEAD_OK;
 }
 
+// Scratch of grpo_head_logp_noalloc: a file-scope device array, one copy per GPU,
+// held until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: kernels and copies get the address hipGetSymbolAddress
+// returns for the current device, looked up once per device and kept.
+constexpr size_t kNoAllocScratchBytes = GRPO_HEAD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (the symbol lookup allocates
+// nothing: the array is part of the loaded code object).
+int noalloc_scratch(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "device %d beyond the %d the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(GRPO_HEAD_HIP_ERROR, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return GRPO_HEAD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -429,6 +462,38 @@ int grpo_head_logp(const grpo_head_params* p, const void* H, const void* W, cons
                 L.fwd_bytes);
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
+  rc = run_logp(p, L, w, H, W, y, mask, logp, lse, s);
+  if (rc) return rc;
+  if (p->validate) {
+    gh::ValidateArgs va{p->n_tokens, 0, p->v_real, p->ignore_index, y, mask, nullptr,
+                        lse, logp, nullptr, nullptr, nullptr, (uint32_t*)(w + L.flags)};
+    hipError_t e = gh::launch_validate(va, s);
+    if (e != hipSuccess) return hip_fail(e, "validation kernel");
+    return finish_validation((uint32_t*)(w + L.flags), s, false);
+  }
+  return ok();
+}
+
+int grpo_head_logp_noalloc(const grpo_head_params* p, const void* H, const void* W,
+                           const int64_t* y, const uint8_t* mask, float* logp, float* lse,
+                           void* stream) {
+  // every argument check runs before any HIP call, as in grpo_head_logp
+  if (!p) return fail(GRPO_HEAD_INVALID_ARGUMENT, "params is NULL");
+  int rc = check_gemm(p);
+  if (rc) return rc;
+  if (p->n_tokens > 0 && (!H || !W || !y || !logp || !lse))
+    return fail(GRPO_HEAD_INVALID_ARGUMENT, "a required buffer is NULL");
+  const gh::WsLayout L = logp_layout(p);
+  if (L.fwd_bytes > kNoAllocScratchBytes)
+    return fail(GRPO_HEAD_INVALID_ARGUMENT,
+                "this problem needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use grpo_head_logp with a workspace)",
+                L.fwd_bytes, kNoAllocScratchBytes);
+  if (p->n_tokens == 0) return ok();
+  char* w = nullptr;
+  rc = noalloc_scratch(&w);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
   rc = run_logp(p, L, w, H, W, y, mask, logp, lse, s);
   if (rc) return rc;
   if (p->validate) {

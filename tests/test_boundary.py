@@ -196,3 +196,21 @@ def test_segment_reduce_rejects_fixed_constant():
                                    ws_bytes=1 << 30, stream=0)
         assert e.value.status == 1 and "fixed_constant" in str(e.value)
     assert gb.segment_workspace_size(P(level="token", beta=0.0)) > 0
+
+
+def test_noalloc_logp_rejects_on_the_host():
+    # argument checks run before any HIP call: a NULL buffer or a problem whose
+    # scratch exceeds the static array is rejected with status 1, nothing enqueued
+    p = gb.make_params(n_tokens=20000, d_model=4096, v_real=151936, v_rows=152064, n_seqs=0,
+                       dtype="bf16")
+    assert gb.logp_workspace_size(p) > gb.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(gb.GrpoHeadError) as e:
+        gb.grpo_head_logp_noalloc(p, 1, 1, 1, None, 1, 1, stream=0)
+    assert e.value.status == 1 and "scratch" in str(e.value)
+    q = gb.make_params(n_tokens=8192, d_model=4096, v_real=151936, v_rows=152064, n_seqs=0,
+                       dtype="bf16")
+    assert gb.logp_workspace_size(q) <= gb.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(gb.GrpoHeadError) as e:
+        gb.grpo_head_logp_noalloc(q, 1, 1, None, None, 1, 1, stream=0)
+    assert e.value.status == 1
+    assert gb.lib.grpo_head_logp_noalloc(None, 1, 1, 1, None, 1, 1, None) == 1
