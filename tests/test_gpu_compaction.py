@@ -117,3 +117,22 @@ def test_compacted_backward_is_bitwise_repeatable(gb):
     b = S.run(gb, inp, d, keep_device=True, chunk_tokens=512)
     for k in a:
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("chunk", [0, 66560])
+def test_many_compaction_blocks(gb, chunk):
+    """A chunk of 70000 tokens has 69 compaction blocks of 1024, beyond the 64 for
+    which each block sums the counts before it itself: the block offsets then come
+    from the scan kernel.  30% of the tokens are masked, scattered over every
+    block; with chunks of 66560 tokens the first chunk takes the scan (65 blocks)
+    and the second the in-block sum."""
+    print(f"70000 tokens, chunk {chunk}", flush=True)
+    cfg = dataclasses.replace(CONFIGS[2], n_tokens=70000, seq_len=1000, d_model=64, v_real=300,
+                              v_rows=320, mask_frac=0.3)
+    inp, lp, lse = S.build(cfg)
+    act = _active(inp)
+    got = S.run(gb, inp, chunk_tokens=chunk)
+    exp = S.expect(inp, lp, lse)
+    S.assert_forward(got, exp, "bf16", act)
+    S.assert_backward(got, exp, "bf16", inp["v_real"])
+    assert np.all(got["dH"][~act] == 0.0)
