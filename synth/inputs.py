@@ -207,8 +207,12 @@ def _keep_off_kinks(noise: np.ndarray, kinks, margin: float, groups=None, active
 
 
 def make_inputs(cfg: Workload, seed: int | None = None, *, old_noise: float | None = None,
-                nan_pad_rows: bool = True, threads: int | None = None) -> dict:
+                nan_pad_rows: bool = True, threads: int | None = None,
+                off_kinks: bool = True) -> dict:
     """Draw one workload.  Returns numpy arrays (bf16 operands as uint16 bits).
+
+    off_kinks=False keeps the old-policy noise as drawn, so some ratios sit at or
+    next to a clip boundary (the parity tests of the clip branch near a kink).
 
     Keys: H [N, D], W [V_r, D], y [N] int64, mask [N] uint8 or None, sid [N] int32,
     n_seqs, adv [S] float32, noise_old [N] float64, noise_ref [N] float64 or None,
@@ -247,7 +251,9 @@ def make_inputs(cfg: Workload, seed: int | None = None, *, old_noise: float | No
     sigma_old = cfg.old_noise if old_noise is None else old_noise
     noise_old = _stream(seed, "old").standard_normal(n) * sigma_old
     kinks = [math.log1p(-cfg.eps_low), math.log1p(cfg.eps_high)]
-    if cfg.level == "sequence_gspo":
+    if not off_kinks:
+        pass
+    elif cfg.level == "sequence_gspo":
         noise_old = _keep_off_kinks(noise_old, kinks, 2e-5, groups=lens, active=active)
     else:
         noise_old = _keep_off_kinks(noise_old, kinks, 1e-4)

@@ -1,9 +1,15 @@
-"""Write the fp64 oracle's selected log-prob and LSE for the full-size workloads.
+"""Write the fp64 oracle's results for the full-size workloads.
 
 Calls only the oracle and the seeded generators.  Usage (from the repo root):
     python tests/golden/make_fullsize.py [config index ...]      # default: 3 4
-Each output file records a fingerprint of the regenerated inputs so readers can
-check they rebuilt the same workload.
+For each workload it stores
+  * logp, lse: the selected log-prob and LSE of every token (a full fp64 forward);
+  * sketch_dH [N, k], sketch_dW [V_r, k]: dH U and dW U for k fixed random probe
+    columns U [D, k] (PROBE_SEED), from the oracle's backward on the objective's
+    coefficient with grad_output = 1 -- a summary of every row of both full-size
+    gradients, too large to store whole (dW alone is 5 GB in fp64);
+and a fingerprint of the regenerated inputs so readers can check they rebuilt the
+same workload.
 """
 import hashlib
 import os
@@ -16,9 +22,16 @@ ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__)
 sys.path.insert(0, ROOT)
 
 import oracle  # noqa: E402
-from synth import CONFIGS, make_inputs  # noqa: E402
+from synth import CONFIGS, attach_logprobs, make_inputs  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+PROBE_SEED = 20251203
+PROBES = 4
+
+
+def probes(d_model: int) -> np.ndarray:
+    """The [D, PROBES] Gaussian probe columns of the gradient sketches."""
+    return np.random.Generator(np.random.PCG64(PROBE_SEED)).standard_normal((d_model, PROBES))
 
 
 def fingerprint(inp: dict) -> str:
@@ -45,7 +58,13 @@ def main(indices):
         act = oracle.active_tokens(inp["y"], inp["mask"], inp["ignore_index"])
         logp, lse = oracle.forward(inp["H"], inp["W"], inp["y"], act, inp["v_real"],
                                    inp["inv_tau"], inp["dtype"], block=256)
+        print(f"{cfg.name}: forward {time.time() - t0:.1f} s", flush=True)
+        obj = oracle.objective(attach_logprobs(inp, logp), logp)
+        sH, sW = oracle.backward_sketch(inp["H"], inp["W"], inp["y"], act, lse, obj["coef"],
+                                        probes(cfg.d_model), inp["v_real"], inp["inv_tau"], 1.0,
+                                        inp["dtype"], block=256)
         np.savez_compressed(path_for(i), logp=logp, lse=lse,
+                            sketch_dH=sH.astype(np.float32), sketch_dW=sW.astype(np.float32),
                             fingerprint=np.array(fingerprint(inp)))
         print(f"{cfg.name}: {time.time() - t0:.1f} s", flush=True)
 
