@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=3072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--clock-seconds", type=float, default=4.0,
+                    help="seconds of extra steps during which the shader clock is sampled")
     ap.add_argument("--steps-only", action="store_true",
                     help="time the steps only (no log-prob entry, shard or variant timings): "
                          "for profiler runs whose per-kernel records should hold step "
@@ -59,21 +61,79 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
-def stored_traffic(workload: str, kernel_stage: str):
-    """HBM bytes per launch of the given stage's kernel from the committed counter
-    summary (FETCH_SIZE / WRITE_SIZE, copy-calibrated), or None when there is no
-    summary or the kernels changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+def stored_counters(workload: str):
+    """The committed per-kernel counter record of this workload
+    (profiles/counters_<workload>.json: copy-calibrated FETCH_SIZE / WRITE_SIZE,
+    executed bf16 MFMA ops, MFMA busy cycles, clock), or None when there is none or
+    the kernels changed since it was taken (its source digest differs)."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
     if rec.get("source_sha256") != source_digest():
         return None
-    k = rec.get("kernels", {}).get(kernel_stage)
+    return rec
+
+
+def stored_traffic(rec, kernel_stage: str):
+    """HBM bytes (fetched + written) per launch of a stage's kernel, or None."""
+    k = (rec or {}).get("kernels", {}).get(kernel_stage)
     if k is None:
         return None
     return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def sample_clock(step, seconds: float, torch):
+    """Measured shader clock while the step runs back to back: the SMU's current
+    gfx clock of each XCD (amdsmi gpu metrics, refreshed about once a second),
+    sampled every 50 ms over `seconds` of steps after one second of ramp-up.
+    Returns a dict, or the reason it could not be read."""
+    import threading
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        amdsmi.amdsmi_get_gpu_metrics_info(h)
+    except Exception as e:          # noqa: BLE001 - any failure means no telemetry
+        return {"mhz": None, "source": f"amdsmi unavailable: {type(e).__name__}: {e}"}
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        t_start = time.perf_counter()
+        while not stop.is_set():
+            if time.perf_counter() - t_start >= 1.0:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                xcd = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int)]
+                if xcd:
+                    samples.append(xcd)
+            time.sleep(0.05)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds + 1.0:
+        step()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    try:
+        amdsmi.amdsmi_shut_down()
+    except Exception:               # noqa: BLE001
+        pass
+    if not samples:
+        return {"mhz": None, "source": "amdsmi gave no gfx clock readings"}
+    arr = np.asarray(samples, dtype=np.float64)
+    return {"mhz": round(float(arr.mean()), 1), "per_xcd_mhz": [round(float(v), 1) for v in
+                                                                 arr.mean(axis=0)],
+            "min_mhz": float(arr.min()), "max_mhz": float(arr.max()),
+            "samples": int(len(arr)), "steps": n,
+            "source": "amdsmi current_gfxclks (SMU telemetry) sampled every 50 ms while "
+                      f"the same step ran back to back for {seconds:.0f} s after 1 s of ramp-up"}
 
 
 def policy_logp(workload: str):
@@ -156,10 +216,20 @@ def cpu_baseline(inp, n_tok):
     oracle.backward(inp["H"][:s], inp["W"], y, act, lse, obj["coef"], inp["v_real"],
                     inp["inv_tau"], 1.0, inp["dtype"], block=256)
     dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                   if p.get("user_api") == "blas"] or [1])
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(s / dt, 2), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "host_cpus": os.cpu_count(),
+            "blas": ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in blas) or None,
             "sample": f"first {s} of {inp['n_tokens']} tokens of the same workload as one batch "
                       f"(full D and V): fp64 forward + objective + backward, {dt:.1f} s"}
 
@@ -240,6 +310,8 @@ def main():
 
     extra = {} if args.steps_only else extra_timings(args, gb, p, d, head, inp, cfg, dH, dW,
                                                      stream, torch)
+    if not args.steps_only:
+        extra["clock"] = sample_clock(step, args.clock_seconds, torch)
     stages = {}
     for name, (a, b) in gb.STAGES.items():
         stages[name] = float(np.mean([hev.elapsed_ms(evs[k][a], evs[k][b]) for k in range(K)]))
@@ -354,6 +426,41 @@ def extra_timings(args, gb, p, d, head, inp, cfg, dH, dW, stream, torch):
     }
 
 
+def epilogue_hbm(cfg, inp, N, D, V, n_live, stages):
+    """HBM rate of the stages around the matrix-core launches: algorithmic bytes
+    (each operand read once, each result written once) over the stage's event time.
+
+      fwd_tail      target logits (an H row and a W row per active token, the target
+                    id and mask) and the ordered merge (every tile partial, the target
+                    logit, writing logp and lse)
+      fwd_objective logp, old and reference log-probs, mask and sequence id read,
+                    the coefficient written (per-sequence sums are a few KB)
+      bwd_prep      row compaction (mask, coefficient, LSE read; row index, row
+                    position and the (g, lse) pair written), the live H rows read and
+                    written twice (as rows and transposed), dead tokens' dH rows zeroed
+      bwd_target    the target element of each live dlogits row: an H row and a W row
+    """
+    esz = 2 if cfg.dtype == "bf16" else 4
+    n_vt = -(-V // 256)
+    active = int(np.count_nonzero(inp["mask"])) if inp["mask"] is not None else N
+    has_ref = inp["ref_logp"] is not None
+    ncp = -(-n_live // 256) * 256
+    stage_bytes = {
+        "fwd_tail": active * (2 * D * esz + 8 + 1 + 4) + N * (n_vt * 8 + 8 + 1 + 4 + 8),
+        "fwd_objective": N * (4 + 4 + (4 if has_ref else 0) + 1 + 4 + 4),
+        "bwd_prep": N * (1 + 4 + 4 + 4) + n_live * (4 + 8) + n_live * D * esz
+                    + 2 * ncp * D * esz + (N - n_live) * D * 4,
+        "bwd_target": n_live * (2 * D * esz + 8 + 4 + 4 + esz),
+    }
+    out = {}
+    for k, b in stage_bytes.items():
+        if k in stages and stages[k] > 0:
+            gbs = b / (stages[k] / 1e3) / 1e9
+            out[k] = {"ms": round(stages[k], 4), "bytes": int(b), "GBps": round(gbs, 1),
+                      "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    return out
+
+
 def report(args, cfg, inp, N, D, V, n_live, K, ms_step, value, wall, stages, per_step, extra):
     """Print the JSON line."""
     from lm_head_selected_amd import binding as gb
@@ -363,19 +470,39 @@ def report(args, cfg, inp, N, D, V, n_live, K, ms_step, value, wall, stages, per
     # (the gradient launch runs both products, dH and dW: twice that)
     launch_flops = {"fwd_tiles": 2.0 * N * D * V, "bwd_dlogits": 2.0 * n_live * D * V,
                     "bwd_grads": 4.0 * n_live * D * V}
-    gemm = {s: {"ms": round(stages[s], 3),
-                "tflops": round(launch_flops[s] / (stages[s] / 1e3) / 1e12, 1)}
-            for s in gb.GEMM_STAGES}
+    counters = stored_counters(cfg.name)
+    gemm = {}
+    for s in gb.GEMM_STAGES:
+        tf = launch_flops[s] / (stages[s] / 1e3) / 1e12
+        gemm[s] = {"ms": round(stages[s], 3), "tflops": round(tf, 1),
+                   "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        k = (counters or {}).get("kernels", {}).get(s)
+        if k and k.get("mfma_flops"):
+            # the matrix-core work the launch executed (the counter counts every MFMA,
+            # padding rows and columns of partial tiles included), over the same time
+            ex = k["mfma_flops"] / (stages[s] / 1e3) / 1e12
+            gemm[s].update(executed_flops=k["mfma_flops"], tflops_executed=round(ex, 1),
+                           frac_of_peak_executed=round(ex / PEAK_BF16_TFLOPS, 4),
+                           mfma_busy=k.get("mfma_busy"), clock_ghz=k.get("clock_ghz"))
     dom = max(gb.GEMM_STAGES, key=lambda s: stages[s])
     achieved = launch_flops[dom] / (stages[dom] / 1e3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": stored_traffic(cfg.name, dom),
+                "traffic": stored_traffic(counters, dom),
                 "kernel": gb.GEMM_STAGES[dom], "stage": dom,
                 "flops_per_launch": launch_flops[dom], "launch_ms": round(stages[dom], 3)}
+    if gemm[dom].get("executed_flops"):
+        roofline["counters"] = {
+            "executed_flops_per_launch": gemm[dom]["executed_flops"],
+            "achieved_executed": gemm[dom]["tflops_executed"],
+            "frac_executed": gemm[dom]["frac_of_peak_executed"],
+            "mfma_busy": gemm[dom]["mfma_busy"], "clock_ghz": gemm[dom]["clock_ghz"],
+            "source": f"profiles/counters_{cfg.name}.json (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, "
+                      "SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE; same kernel sources)"}
 
     flops_8nvd = 8.0 * N * V * D
     flops_exec = (2.0 * N + 6.0 * n_live) * V * D
+    epilogue = epilogue_hbm(cfg, inp, N, D, V, n_live, stages)
     out = {
         "metric": "tokens/s fwd+bwd fused GRPO head loss + % bf16 MFMA peak, D=4096 V=151936",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
@@ -386,13 +513,16 @@ def report(args, cfg, inp, N, D, V, n_live, K, ms_step, value, wall, stages, per
                    "reduction": cfg.reduction, "level": cfg.level, "parallelism": "none"},
         "step_ms_median": round(statistics.median(per_step), 3),
         "step_ms_min": round(min(per_step), 3),
-        "tflops_8nvd": round(flops_8nvd / (ms_step / 1e3) / 1e12, 1),
-        "tflops_6nvd": round(0.75 * flops_8nvd / (ms_step / 1e3) / 1e12, 1),
-        "frac_of_peak_8nvd": round(flops_8nvd / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "backward_rows": n_live,
         "tflops_executed": round(flops_exec / (ms_step / 1e3) / 1e12, 1),
         "frac_of_peak_executed": round(flops_exec / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        # nominal accountings: they credit the backward's products for every token,
+        # also the N - backward_rows tokens whose dlogits rows are zero and never run
+        "nominal": {"tflops_8nvd": round(flops_8nvd / (ms_step / 1e3) / 1e12, 1),
+                    "tflops_6nvd_model": round(0.75 * flops_8nvd / (ms_step / 1e3) / 1e12, 1),
+                    "note": "credits skipped rows; not a measure of the executed work"},
         "gemm_launches": gemm,
+        "epilogue_hbm": epilogue,
         "stages_ms": {k: round(v, 3) for k, v in stages.items()},
         "wall_s": round(wall, 3),
         "roofline": roofline,
