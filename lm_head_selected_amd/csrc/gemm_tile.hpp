@@ -216,6 +216,14 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Wait until every LDS access of this wave has completed (s_waitcnt lgkmcnt(0)),
+// written as the builtin so that the compiler's own wait tracking sees it.
+__device__ __forceinline__ void lgkm_drain() {
+  // gfx9 s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8];
+  // vmcnt and expcnt at their maxima (no wait), lgkmcnt 0
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+}
+
 // Workgroup barrier for the K pipeline.  __syncthreads() would also drain every
 // in-flight direct-to-LDS load (its fence waits for vmcnt(0)); here the caller
 // waits for exactly the stage it needs, and this wave's LDS reads are drained
@@ -406,6 +414,12 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   wait_vm<(kSolo ? 4 : 2) * kLoads>();   // stage 0 landed; stage 1 may be in flight
   pipe_barrier();
   read_frags(fa0, fb0, 0, 0);
+  // Let these reads land before the loop.  With an MN operand they are 16 LDS
+  // reads, more than the 4-bit LDS counter the compiler's wait tracking follows;
+  // entering the loop with them in flight made it wait for every LDS read
+  // (lgkmcnt(0)) at the head of each K stage, while drained here it emits exact
+  // counts there.  The cost is one LDS round trip per tile.
+  lgkm_drain();
   __builtin_amdgcn_sched_barrier(0);
 
   for (int kt = 0; kt < nk; ++kt) {
