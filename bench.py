@@ -435,10 +435,11 @@ def epilogue_hbm(cfg, inp, N, D, V, n_live, stages):
                     logit, writing logp and lse)
       fwd_objective logp, old and reference log-probs, mask and sequence id read,
                     the coefficient written (per-sequence sums are a few KB)
-      bwd_prep      row compaction (mask, coefficient, LSE read; row index, row
-                    position and the (g, lse) pair written), the live H rows read and
-                    written twice (as rows and transposed), dead tokens' dH rows zeroed
-      bwd_target    the target element of each live dlogits row: an H row and a W row
+      bwd_prep      row compaction (mask, coefficient, LSE read; row position
+                    written per token; row index, (g, lse) pair and target id per
+                    live row), the live H rows read and written twice (as rows and
+                    transposed), the dead tokens' dH rows zeroed
+    (The backward's target elements come out of the dlogits tile epilogue.)
     """
     esz = 2 if cfg.dtype == "bf16" else 4
     n_vt = -(-V // 256)
@@ -448,9 +449,8 @@ def epilogue_hbm(cfg, inp, N, D, V, n_live, stages):
     stage_bytes = {
         "fwd_tail": active * (2 * D * esz + 8 + 1 + 4) + N * (n_vt * 8 + 8 + 1 + 4 + 8),
         "fwd_objective": N * (4 + 4 + (4 if has_ref else 0) + 1 + 4 + 4),
-        "bwd_prep": N * (1 + 4 + 4 + 4) + n_live * (4 + 8) + n_live * D * esz
+        "bwd_prep": N * (1 + 4 + 4 + 4) + n_live * (4 + 8 + 8 + 4) + n_live * D * esz
                     + 2 * ncp * D * esz + (N - n_live) * D * 4,
-        "bwd_target": n_live * (2 * D * esz + 8 + 4 + 4 + esz),
     }
     out = {}
     for k, b in stage_bytes.items():

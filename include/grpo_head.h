@@ -360,10 +360,10 @@ int grpo_group_advantage(const float* rewards, int64_t n_seqs, int64_t group_siz
  *                  objective stage (grpo_head_logp records [0]-[2] the same way);
  *   grpo_head_bwd: [4] at entry, [5] just before a token chunk's dlogits tile
  *                  launch (after the row compaction and the H gather), [6] after
- *                  that launch, [7] after the target-element fix-up, [8] after
+ *                  that launch (which also forms the target elements), [7] after
  *                  the launch of the two gradient products, dH and dW (with
- *                  several chunks, [5]-[8] describe the last one).
- * So [0]-[1], [5]-[6] and [7]-[8] each bracket one matrix-core launch.
+ *                  several chunks, [5]-[7] describe the last one).
+ * So [0]-[1], [5]-[6] and [6]-[7] each bracket one matrix-core launch.
  * Returns GRPO_HEAD_INVALID_ARGUMENT if n_events < 0 or > 16. */
 int grpo_head_set_stage_events(void* const* events, int n_events);
 

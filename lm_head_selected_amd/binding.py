@@ -33,10 +33,9 @@ EXPORTS = ("grpo_head_fwd_workspace_size", "grpo_head_workspace_size",
 NOALLOC_SCRATCH_BYTES = 64 << 20   # GRPO_HEAD_NOALLOC_SCRATCH_BYTES
 
 # stage-event slots recorded by grpo_head_fwd / grpo_head_bwd
-N_STAGE_EVENTS = 9
+N_STAGE_EVENTS = 8
 STAGES = {"fwd_tiles": (0, 1), "fwd_tail": (1, 2), "fwd_objective": (2, 3),
-          "bwd_prep": (4, 5), "bwd_dlogits": (5, 6), "bwd_target": (6, 7),
-          "bwd_grads": (7, 8)}
+          "bwd_prep": (4, 5), "bwd_dlogits": (5, 6), "bwd_grads": (6, 7)}
 # stages that are exactly one matrix-core launch, with that launch's kernel symbol stem
 GEMM_STAGES = {"fwd_tiles": "fwd_tile_chain_kernel", "bwd_dlogits": "dlogits_kernel",
                "bwd_grads": "grad_products_kernel<__bf16, float>"}

@@ -18,9 +18,9 @@
 //   2. gather_rows_kernel : the live H rows, as Hg[r][d] and transposed, blocked
 //                           by 64 rows, HT[r / 64][d][r % 64]
 //      zero_dead_rows_kernel: dH rows of the dead tokens = 0
-//   3. dlogits_kernel     : -g_t p_tv tile on the matrix cores -> dz (bf16, nearest
-//                           even, on the bf16 path; fp32 on the fp32 path)
-//      target_logit_kernel: rewrites dz[r][y_t] = g_t (1 - p_t,y_t)
+//   3. dlogits_kernel     : g_t (1[v == y_t] - p_tv) tile on the matrix cores -> dz
+//                           (bf16, nearest even, on the bf16 path; fp32 on the fp32
+//                           path)
 //   4. grad_products_kernel, one launch of two products:
 //      dH[rows[r]][d] = sum_v dz[r][v] W[v][d]
 //      (M = r: dz K-contiguous; N = d: W read MN-contiguous), and
@@ -71,6 +71,7 @@ struct DlogitsArgs {
   int64_t dz_rows;
   int group_m;
   const int32_t* live;            // live row count (device); token tiles past it are skipped
+  const int32_t* ytg;             // [dz_rows] target id of each row, -1 where there is none
 };
 
 // Row compaction of one chunk (blocks of kCompactBlock tokens, one per thread).
@@ -86,6 +87,8 @@ struct CompactArgs {
   float2* gl;         // [n_pad] (g_t, lse_t log2 e) of compact row r; (0, 0) past them
   int32_t* bbase;     // [blocks] live tokens before each block, or null: each block sums
                       // the counts before it itself (few blocks)
+  int64_t v_real;
+  int32_t* ytg;       // [n_pad] target id of compact row r if in [0, v_real), else -1
 };
 
 // g_t = grad_output * coef_t / tau for an active token, 0 otherwise.  A token is
@@ -169,6 +172,8 @@ __global__ __launch_bounds__(kCompactBlock) void compact_kernel(CompactArgs a) {
     if (lv) {
       a.rows[pos] = (int32_t)t;
       a.gl[pos] = make_float2(g, a.lse[t] * kLog2e);
+      const int64_t yy = a.y[t];   // a live token is active: its target is defined
+      a.ytg[pos] = (yy >= 0 && yy < a.v_real) ? (int32_t)yy : -1;
     }
   }
   if (blockIdx.x == gridDim.x - 1) {
@@ -178,12 +183,14 @@ __global__ __launch_bounds__(kCompactBlock) void compact_kernel(CompactArgs a) {
     for (int64_t r = total + threadIdx.x; r < a.n_pad; r += kCompactBlock) {
       a.rows[r] = -1;
       a.gl[r] = make_float2(0.0f, 0.0f);
+      a.ytg[r] = -1;
     }
   }
 }
 
-// dz[r][v] = -g_r p_rv over the tile, for live row r (the target element is
-// rewritten afterwards by the target-logit kernel).  On the tile holding the
+// dz[r][v] = g_r (1[v == y_r] - p_rv) over the tile, for live row r: the target
+// element is formed by the one lane that holds it, behind a wave-wide test (a tile
+// holds about 256 * 256 / V targets), so the common path is -g p.  On the tile holding the
 // vocabulary's ragged end the padded columns v >= v_real are set to -inf before
 // the exponential, so their dz is zero: their W rows load as zeros, and a zero
 // logit there would otherwise give -g 2^(-lse2), which overflows for a very
@@ -227,20 +234,23 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
   // 32-byte segment s of LDS row t sits at segment s ^ (t & 15)
   char* L = lds;
 
-#pragma unroll
-  for (int j = 0; j < kBJ; ++j) {
-    const int tl = wn * (kTile / kWN) + j * 16 + (lane & 15);   // tile-local token
-    // (cast the whole vector: clang miscompiles bit_cast of a single vector element)
-    const f32x2 glv = __builtin_bit_cast(
-        f32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, (uint32_t)((t0 + tl) * 8), 0, 0));
-    const float g = glv[0];
-    const float lse2 = glv[1];
+  // target id of the lane's row; -1 past the live rows (cleared by the compaction)
+  const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.ytg, (uint32_t)(a.dz_rows * 4));
+  const int qg = lane >> 4;
+  // the tile's elements of column block j; kFix: one lane of the wave holds a
+  // target element, rel its row within the wave's 128 rows
+  auto column = [&](int j, int tl, float g, float lse2, int32_t rel, bool own, auto fix) {
+    constexpr bool kFix = decltype(fix)::value;
     char* rowp = tile + (int64_t)tl * 256 * esz;
 #pragma unroll
     for (int i = 0; i < kBI; ++i) {
       float d[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) d[e] = -g * fast_exp2(acc[i][j][e] * c2 - lse2);
+      for (int e = 0; e < 4; ++e) {
+        const float p = fast_exp2(acc[i][j][e] * c2 - lse2);
+        d[e] = -g * p;
+        if (kFix) d[e] = (own && rel == i * 16 + qg * 4 + e) ? g * (1.0f - p) : d[e];
+      }
       const int v = vl + i * 16;                                 // 4 consecutive v
       if (sizeof(T) == 2) {
         const bf16x4 q = {(__bf16)d[0], (__bf16)d[1], (__bf16)d[2], (__bf16)d[3]};
@@ -251,6 +261,24 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
         Store4<T>::run(rowp + v * esz, d[0], d[1], d[2], d[3]);
       }
     }
+  };
+
+#pragma unroll
+  for (int j = 0; j < kBJ; ++j) {
+    const int tl = wn * (kTile / kWN) + j * 16 + (lane & 15);   // tile-local token
+    // (cast the whole vector: clang miscompiles bit_cast of a single vector element)
+    const f32x2 glv = __builtin_bit_cast(
+        f32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, (uint32_t)((t0 + tl) * 8), 0, 0));
+    const float g = glv[0];
+    const float lse2 = glv[1];
+    const int32_t yt = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ry, (uint32_t)((t0 + tl) * 4),
+                                                                    0, 0);
+    const int32_t rel = yt - (int32_t)(v0 + wm * (kTile / kWM));
+    const bool own = yt >= 0 && (uint32_t)rel < (uint32_t)(kTile / kWM) && ((rel >> 2) & 3) == qg;
+    if (__builtin_amdgcn_ballot_w64(own) != 0)
+      column(j, tl, g, lse2, rel, own, std::true_type{});
+    else
+      column(j, tl, g, lse2, rel, own, std::false_type{});
   }
   if (sizeof(T) == 2) {
     __syncthreads();
@@ -535,8 +563,9 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     // up to 64 blocks each block sums the counts before it in one pass of a wave;
     // beyond that a scan kernel forms the block offsets first
     int32_t* bbase = nb > 64 ? bcnt + nb : nullptr;
+    int32_t* ytg = (int32_t*)(a.ws + L.ytg);
     const CompactArgs ca{a.y + c0, cmask, a.ignore_index, a.coef + c0, a.lse + c0, a.grad_output,
-                         a.inv_tau, nc, ncp, bcnt, live, rows, rowpos, gl, bbase};
+                         a.inv_tau, nc, ncp, bcnt, live, rows, rowpos, gl, bbase, a.v_real, ytg};
     hipLaunchKernelGGL(live_count_kernel, dim3(nb), dim3(kCompactBlock), 0, s, ca);
     if (bbase)
       hipLaunchKernelGGL(block_scan_kernel, dim3(1), dim3(kCompactBlock), 0, s,
@@ -549,18 +578,11 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(zero_dead_rows_kernel<O>, dim3((unsigned)ceil_div(nc, 4)), dim3(256), 0, s,
                        (const int32_t*)rowpos, nc, D, dH + c0 * D);
 
-    DlogitsArgs d{a.W, hg, gl, nc, D, a.v_real, a.inv_tau, dz, R, a.group_dlogits, live};
+    DlogitsArgs d{a.W, hg, gl, nc, D, a.v_real, a.inv_tau, dz, R, a.group_dlogits, live, ytg};
     ev.mark(5, s);
     hipLaunchKernelGGL(dlogits_kernel<T>, dim3(tiles_v * tiles_t), dim3(kThreads), 0, s, d,
                        tiles_v, tiles_t);
     ev.mark(6, s);
-    TargetArgs fx{Hc, a.W, a.y + c0, cmask, nc, D, a.v_real, a.ignore_index, a.inv_tau, 1,
-                  nullptr, a.lse + c0, a.coef + c0, a.grad_output, dz, R};
-    fx.rows = rows;
-    fx.live = live;
-    hipError_t e0 = launch_target_logit(sizeof(T) == 2 ? 0 : 1, fx, s);
-    if (e0 != hipSuccess) return e0;
-    ev.mark(7, s);
 
     // dH rows of the chunk: M = live row r (dz rows), N = d (W read MN-contiguous),
     // K = v; row r goes to token rows[r].  W rows >= v_real are never read (they
@@ -579,7 +601,7 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     const int dh_slots = (int)ceil_div((int64_t)tiles_t * tiles_d, 8) * 8;
     hipLaunchKernelGGL((grad_products_kernel<T, O>), dim3(dh_slots + tiles_d * tiles_v),
                        dim3(kThreads), 0, s, ph, pw, dh_slots, tiles_t, tiles_d, tiles_d, tiles_v);
-    ev.mark(8, s);
+    ev.mark(7, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

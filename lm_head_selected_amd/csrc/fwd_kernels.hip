@@ -158,21 +158,13 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_chain_kernel(FwdTileArgs a,
 
 // One wave per token: z[t, y_t] * inv_tau = inv_tau * sum_d H[t, d] W[y_t, d] for
 // an active token with a target in [0, v_real) (fp32 products and sums; bf16
-// products are exact in fp32).  mode 0 writes it to zy[t]; mode 1 (backward)
-// writes the target element of the dlogits row, g_t (1 - exp(z - lse_t)), over
-// the -g_t p value the tile wrote there; with a row list the grid walks the
-// compacted dlogits rows, row r holding token rows[r].
+// products are exact in fp32), written to zy[t] (mode 0), or for a vocabulary
+// shard (mode 2) zy[t] for every token, 0 when the target lies elsewhere.
 template <typename T>
 __global__ __launch_bounds__(256) void target_logit_kernel(TargetArgs a) {
   const int lane = threadIdx.x & 63;
-  // r: the token, or (mode 1 on compacted rows) the dlogits row of token rows[r]
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int64_t t = r;
-  if (a.rows) {
-    if (r >= (int64_t)*a.live) return;
-    t = a.rows[r];
-  }
-  if (t < 0 || t >= a.n_tokens) return;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.n_tokens) return;
   const bool act = token_active(a.mask, a.y, a.ignore_index, t);
   const int64_t yy = act ? a.y[t] : -1;
   const int64_t yl = yy - a.v_begin;                 // row within this W
@@ -206,18 +198,7 @@ __global__ __launch_bounds__(256) void target_logit_kernel(TargetArgs a) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
   if (lane != 0) return;
-  const float z = acc * a.inv_tau;
-  if (a.mode != 1) {
-    a.zy[t] = z;
-  } else {
-    const float g = a.grad_output ? *a.grad_output * a.coef[t] * a.inv_tau
-                                  : a.coef[t] * a.inv_tau;
-    const float v = g * (1.0f - fast_exp2((z - a.lse[t]) * kLog2e));
-    // dz is v-tiled: [vocabulary / 256][dz_rows][256]
-    char* p = (char*)a.dz + vtiled_offset(r, yy, a.dz_rows, (int64_t)sizeof(T));
-    if (sizeof(T) == 2) *(__bf16*)p = (__bf16)v;
-    else *(float*)p = v;
-  }
+  a.zy[t] = acc * a.inv_tau;
 }
 
 // (M, S) <- (M, S) (+) (m, s): the merge of two (max, sumexp) partials in base-2

@@ -144,6 +144,7 @@ gh::WsLayout layout(const grpo_head_params* p, bool with_gemm = true) {
   L.rows = take((size_t)chunk * 4);
   L.rowpos = take((size_t)chunk * 4);
   L.hg = take((size_t)chunk * D * esz);       // the chunk's live H rows
+  L.ytg = take((size_t)chunk * 4);            // target id of each compact row
   L.bwd_bytes = off > L.fwd_bytes ? off : L.fwd_bytes;
   return L;
 }
@@ -194,7 +195,7 @@ int run_logp(const grpo_head_params* p, const gh::WsLayout& L, char* w, const vo
   hipError_t e = gh::launch_fwd_tiles(p->dtype, fa, L.n_vt, g_marks, s);
   if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
   gh::TargetArgs ta{H, W, y, mask, p->n_tokens, p->d_model, p->v_real, p->ignore_index,
-                    p->inv_tau, 0, (float*)(w + L.zy), nullptr, nullptr, nullptr, nullptr, 0};
+                    p->inv_tau, 0, (float*)(w + L.zy)};
   e = gh::launch_target_logit(p->dtype, ta, s);
   if (e != hipSuccess) return hip_fail(e, "target logit kernel");
   gh::MergeArgs ma{(const float2*)(w + L.partials), (const float*)(w + L.zy), y, mask,
@@ -347,7 +348,7 @@ int grpo_head_shard_partials(const grpo_head_params* p, int64_t v_begin, int64_t
     if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
   }
   gh::TargetArgs ta{H, W_shard, y, mask, p->n_tokens, p->d_model, rows, p->ignore_index,
-                    p->inv_tau, 2, zy, nullptr, nullptr, nullptr, nullptr, 0, v_begin};
+                    p->inv_tau, 2, zy, v_begin};
   hipError_t e = gh::launch_target_logit(p->dtype, ta, s);
   if (e != hipSuccess) return hip_fail(e, "target logit kernel");
   return ok();

@@ -23,8 +23,9 @@ struct WsLayout {
   // backward (reuses the workspace from offset 0)
   size_t bflags = 0, gl = 0, dz = 0, ht = 0;
   // backward row compaction: per-block live counts, the live count, the live rows'
-  // token indices, every token's compact row (-1 if dead) and the gathered H rows
-  size_t bcnt = 0, live = 0, rows = 0, rowpos = 0, hg = 0;
+  // token indices, every token's compact row (-1 if dead), the gathered H rows and
+  // each compact row's target id
+  size_t bcnt = 0, live = 0, rows = 0, rowpos = 0, hg = 0, ytg = 0;
   size_t bwd_bytes = 0;
   int64_t n_vt = 0;        // vocabulary tiles covering [0, v_real)
   int64_t v_k = 0;         // n_vt * 256: vocabulary extent of the dlogits buffer
@@ -41,22 +42,17 @@ struct FwdTileArgs {
   float2* partials;  // [n_vt][n_tokens]
   int group_m;
 };
-// Target-logit gather (mode 0: zy[t]), the backward's target-element fix-up
-// (mode 1: dz[t][y_t] = g_t (1 - p_t,y); pointers already offset to the chunk), or
-// a vocabulary shard's gather (mode 2).
+// Target-logit gather (mode 0: zy[t] for the active tokens with a target in
+// [0, v_real)), or a vocabulary shard's gather (mode 2: W holds rows
+// [v_begin, v_begin + v_real) and zy[t] is written for every token, 0 unless y_t
+// lies in the shard).
 struct TargetArgs {
   const void* H; const void* W; const int64_t* y; const uint8_t* mask;
   int64_t n_tokens, d_model, v_real, ignore_index;
   float inv_tau;
   int mode;
   float* zy;
-  const float* lse; const float* coef; const float* grad_output;
-  void* dz; int64_t dz_rows;   // dlogits buffer (v-tiled, dz_rows rows per group)
-  // mode 2 (a vocabulary shard's gather): W holds rows [v_begin, v_begin + v_real)
-  // and zy[t] is written for every token, 0 unless y_t lies in the shard
   int64_t v_begin = 0;
-  // mode 1 on compacted rows: dz row r < *live holds token rows[r] (else dz row = t)
-  const int32_t* rows = nullptr; const int32_t* live = nullptr;
 };
 struct MergeArgs {
   const float2* partials; const float* zy; const int64_t* y; const uint8_t* mask;
