@@ -34,7 +34,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_8b_head_grpo_n8192")
     ap.add_argument("--cpu-tokens", type=int, default=3072)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -309,7 +309,7 @@ def main():
     value = N / (ms_step / 1e3)
 
     extra = {} if args.steps_only else extra_timings(args, gb, p, d, head, inp, cfg, dH, dW,
-                                                     stream, torch)
+                                                     stream, n_live, torch)
     if not args.steps_only:
         extra["clock"] = sample_clock(step, args.clock_seconds, torch)
     stages = {}
@@ -320,7 +320,7 @@ def main():
     report(args, cfg, inp, N, D, V, n_live, K, ms_step, value, wall, stages, per_step, extra)
 
 
-def extra_timings(args, gb, p, d, head, inp, cfg, dH, dW, stream, torch):
+def extra_timings(args, gb, p, d, head, inp, cfg, dH, dW, stream, n_live, torch):
     """The entry points and variants timed after the steps, on the same inputs."""
     N, D, V = cfg.n_tokens, cfg.d_model, cfg.v_real
     dev = d["H"].device
@@ -414,7 +414,9 @@ def extra_timings(args, gb, p, d, head, inp, cfg, dH, dW, stream, torch):
         ms_all = l0.elapsed_time(l1) / K2
     else:
         ms_all = None
+    lib = library_gemms(d, cfg, n_live, K2, torch) if cfg.dtype == "bf16" else None
     return {
+        "library_gemm": lib,
         "logp_entry": {"ms": round(ms_logp, 3), "calls": K2,
                        "tokens_per_s": round(N / (ms_logp / 1e3), 1),
                        "tflops_2nvd": round(2.0 * N * V * D / (ms_logp / 1e3) / 1e12, 1)},
@@ -424,6 +426,42 @@ def extra_timings(args, gb, p, d, head, inp, cfg, dH, dW, stream, torch):
         "tp2_shard_tiles": {"v_rows": v_half, "ms": round(ms_shard, 3),
                             "tflops": round(2.0 * N * v_half * D / (ms_shard / 1e3) / 1e12, 1)},
     }
+
+
+def library_gemms(d, cfg, n_live, reps, torch):
+    """Context, not part of the step: the vendor BLAS (hipBLASLt through
+    torch.matmul) on plain bf16 GEMMs of the step's three contraction shapes, with
+    bf16 outputs and none of the softmax, loss or dlogits work: the logits H W^T
+    (which it writes out, 2 N V_rows bytes), dH = G W and dW = G^T H over the live
+    rows (G random, the dlogits shape).  Timed on torch's current stream."""
+    N, D, Vr = cfg.n_tokens, cfg.d_model, cfg.v_rows
+    H, W = d["H"], d["W"]
+    G = torch.randn(n_live, Vr, device=H.device, dtype=torch.bfloat16) * 1e-3
+    Hl = H[:n_live].contiguous()
+    shapes = {"logits_H_Wt": (H, W.t(), 2.0 * N * Vr * D),
+              "dH_G_W": (G, W, 2.0 * n_live * Vr * D),
+              "dW_Gt_H": (G.t(), Hl, 2.0 * n_live * Vr * D)}
+    out = {"note": "hipBLASLt via torch.matmul, bf16 in and out, plain GEMMs of the same "
+                   "shapes (no softmax, loss or dlogits work); context only",
+           "reps": reps}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total = 0.0
+    for name, (a, b, flops) in shapes.items():
+        c = a @ b
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        total += ms
+        out[name] = {"ms": round(ms, 3), "tflops": round(flops / (ms / 1e3) / 1e12, 1)}
+        del c
+    out["sum_ms"] = round(total, 3)
+    del G, Hl
+    torch.cuda.empty_cache()
+    return out
 
 
 def epilogue_hbm(cfg, inp, N, D, V, n_live, stages):

@@ -88,16 +88,6 @@ __host__ __device__ inline Operand nt_vtiled(const void* base, int64_t rows_pad,
   return Operand{(const char*)base, 256 * esz, 256 * 256 * esz, total_bytes, total_bytes,
                  rows_pad * 256 * esz, shift, 0};
 }
-// The K-blocked layout [K / 64][rows][64 elements] read K-contiguous with rows =
-// its rows: each 64-element block of a row is one (bf16) or two (fp32) stages, and
-// a stage of 256 rows is one contiguous run.  Rows past `rows` of the last tile read
-// the next block's rows; those results are not stored.
-__host__ __device__ inline Operand nt_kblocked(const void* base, int64_t rows, int64_t esz,
-                                              int64_t total_bytes) {
-  const int32_t shift = esz == 2 ? 0 : 1;   // 128-byte stages per 64-element block
-  return Operand{(const char*)base, 64 * esz, 256 * 64 * esz, total_bytes, total_bytes,
-                 rows * 64 * esz, shift, 0};
-}
 // Row-major [k_rows][cols] (pitch bytes per row) read MN-contiguous, K = its rows:
 // K rows >= k_rows and columns >= cols of the last valid row load as zeros.
 __host__ __device__ inline Operand mn_row_major(const void* base, int64_t pitch, int64_t k_rows,
