@@ -88,6 +88,7 @@ struct CompactArgs {
                       // the counts before it itself (few blocks)
   int64_t v_real;
   int32_t* ytg;       // [n_pad] target id of compact row r if in [0, v_real), else -1
+  int32_t* dwq;       // [8] the gradient launch's dW tile queues, cleared here
 };
 
 // g_t = grad_output * coef_t / tau for an active token, 0 otherwise.  A token is
@@ -179,6 +180,7 @@ __global__ __launch_bounds__(kCompactBlock) void compact_kernel(CompactArgs a) {
     int total = base;
     for (int w = 0; w < kCompactWaves; ++w) total += wcnt[w];
     if (threadIdx.x == 0) *a.live = total;
+    if (threadIdx.x < 8) a.dwq[threadIdx.x] = 0;
     for (int64_t r = total + threadIdx.x; r < a.n_pad; r += kCompactBlock) {
       a.rows[r] = -1;
       a.gl[r] = make_float2(0.0f, 0.0f);
@@ -294,9 +296,9 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
 }
 
 // Products with a K-contiguous A and an MN-contiguous B.
-//   kRole 0 (dH): C[m = live row r][n = d] stored row-major at the row's token:
-//                 out[out_rows[m] * ld_out + n];
-//   kRole 1 (dW): C[m = d][n = v] stored as out[n * ld_out + m .. + 3].
+//   dH: C[m = live row r][n = d] stored row-major at the row's token:
+//       out[out_rows[m] * ld_out + n];
+//   dW: C[m = d][n = v] stored as out[n * ld_out + m .. + 3].
 struct ProductArgs {
   Operand A, B;
   int nk;                         // K stages
@@ -306,9 +308,8 @@ struct ProductArgs {
   int64_t zero_from;              // dW rows (N) >= this are written as 0 (padded vocab)
   int accumulate;                 // add to out
   int group_m;
-  // live row count (device): kRole 0 runs the M tiles holding live rows and
-  // writes compact row m to out row out_rows[m]; kRole 1 runs the K stages
-  // covering them
+  // live row count (device): dH runs the M tiles holding live rows and writes
+  // compact row m to out row out_rows[m]; dW runs the K stages covering them
   const int32_t* live;
   const int32_t* out_rows;
 };
@@ -334,79 +335,114 @@ __device__ __forceinline__ void store_out4(__bf16* p, f32x4 v) {
   __builtin_nontemporal_store(__builtin_bit_cast(i32x2, b), (i32x2*)p);
 }
 
-// The dW tile's epilogue: rows n0 .. n0 + 255 (vocabulary), columns m0 .. m0 + 255
-// (hidden), staged through the (now free) pipeline LDS in two halves of 128 rows
-// and written as whole 1 KB row segments.  16-byte chunk c of LDS row r sits at
-// chunk c ^ (r & 15).  Rows >= zero_from are written as zeros; with accumulate
-// the tile is added to what out holds.
+// LDS of the gradient launch: the K pipeline's buffers, then, for the dW tiles,
+// one epilogue slice per wave and a ring of four queued tile ids.
+constexpr int kDwSlice = 2048;                        // bytes per wave
+constexpr int kDwEpiLds = kWaves * kDwSlice;
+constexpr int kGradLds = kGemmLds + kDwEpiLds + 8 * (int)sizeof(int32_t);
+
+__device__ __forceinline__ void lds_store16(lds_t* p, f32x4 v) {
+  *(__attribute__((address_space(3))) f32x4*)p = v;
+}
+__device__ __forceinline__ f32x4 lds_load16(const lds_t* p) {
+  return *(const __attribute__((address_space(3))) f32x4*)p;
+}
+
+// Four output elements at byte offset off of a buffer resource (fp32, or bf16
+// rounded to nearest even); offsets past the resource's range load zeros and
+// store nothing.
+__device__ __forceinline__ f32x4 buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off, float*) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ f32x4 buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off, __bf16*) {
+  const bf16x4 b = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+  return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
+// cache policy 2: non-temporal (see Store4)
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v,
+                                           float*) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 2);
+}
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v,
+                                           __bf16*) {
+  const bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, b), r, off, 0, 2);
+}
+
+// One dW tile's output, rows n0 .. n0 + 255 of out (vocabulary), columns
+// m0 .. m0 + 255 (hidden), written while the next tile's loads are in flight: each
+// wave passes its 128 (hidden) x 64 (vocabulary) sub-tile through its own 2 KB
+// slice of LDS past the pipeline buffers, 16 passes of 16 rows x 32 columns, with
+// no workgroup barrier, and writes each row's 32 columns as one 128-byte run (fp32).
+// Rows >= zero_from are written as zeros; with accumulate the tile is added to
+// what out holds.  Rows >= n_limit and columns >= m_limit lie outside the stores'
+// buffer range and are dropped, so every wave issues the same stores.  In a slice,
+// 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7), so both the writes
+// (16 rows at one chunk) and the reads (8 whole rows) are free of bank conflicts.
 template <typename O>
-__device__ __forceinline__ void store_dw_tile(const f32x4 (&acc)[kBI][kBJ], char* lds, O* out,
-                                              int64_t ld_out, int64_t n0, int64_t m0,
-                                              int64_t n_limit, int64_t m_limit,
-                                              int64_t zero_from, int accumulate) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ void store_dw_tile_wave(const f32x4 (&acc)[kBI][kBJ], lds_t* slice,
+                                                   O* out, int64_t ld_out, int64_t n0,
+                                                   int64_t m0, int64_t n_limit, int64_t m_limit,
+                                                   int64_t zero_from, int accumulate) {
+  // (the lane index made opaque, so that nothing derived from it is hoisted out of
+  // the caller's tile loop, where it would stay live across the K loop)
+  int lane = threadIdx.x & 63;
+  __asm__("" : "+v"(lane));
+  const int wave = threadIdx.x >> 6;
   const int wm = wave / kWN, wn = wave % kWN;
-  float* L = (float*)lds;   // [128][256]
+  int64_t rows = n_limit - n0;
+  rows = rows < 0 ? 0 : (rows > kTile ? kTile : rows);
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(out + n0 * ld_out, (uint32_t)(rows * ld_out * (int64_t)sizeof(O)));
+  const int wr = lane & 15;                 // row written by this lane
+  const int rq = lane >> 4;                 // its 4-column group within a block
+  const int rc = lane & 7;                  // chunk read by this lane
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    if ((wn >> 1) == p) {
+  for (int j = 0; j < kBJ; ++j) {
 #pragma unroll
-      for (int j = 0; j < kBJ; ++j) {
-        const int r = (wn & 1) * 64 + j * 16 + (lane & 15);
+    for (int g = 0; g < kBI / 2; ++g) {     // hidden columns g * 32 .. + 31 of the wave's 128
 #pragma unroll
-        for (int i = 0; i < kBI; ++i) {
-          const int c = (wm * 128 + i * 16 + (lane >> 4) * 4) >> 2;
-          *(f32x4*)(L + r * 256 + ((c ^ (r & 15)) << 2)) = acc[i][j];
-        }
+      for (int u = 0; u < 2; ++u) {
+        const int c = u * 4 + rq;
+        lds_store16(slice + wr * 128 + ((c ^ ((wr >> 1) & 7)) << 4), acc[2 * g + u][j]);
+      }
+      lgkm_drain();
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int rr = u * 8 + (lane >> 3);
+        f32x4 v = lds_load16(slice + rr * 128 + ((rc ^ ((rr >> 1) & 7)) << 4));
+        const int64_t nl = wn * (kTile / kWN) + j * 16 + rr;      // tile-local row
+        const int64_t m = m0 + wm * (kTile / kWM) + g * 32 + rc * 4;
+        const uint32_t off =
+            m < m_limit ? (uint32_t)((nl * ld_out + m) * (int64_t)sizeof(O)) : 0xFFFFFFF0u;
+        if (n0 + nl >= zero_from) v = f32x4{0.f, 0.f, 0.f, 0.f};
+        else if (accumulate) v += buf_load4(r, off, (O*)nullptr);
+        buf_store4(r, off, v, (O*)nullptr);
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = (threadIdx.x >> 6) + 8 * q, c = threadIdx.x & 63;
-      const int64_t n = n0 + p * 128 + r, m = m0 + c * 4;
-      if (n < n_limit && m < m_limit) {
-        f32x4 v = *(const f32x4*)(L + r * 256 + ((c ^ (r & 15)) << 2));
-        O* o = out + n * ld_out + m;
-        if (n >= zero_from) v = f32x4{0.f, 0.f, 0.f, 0.f};
-        else if (accumulate) v += load_out4(o);
-        store_out4(o, v);
-      }
-    }
-    __syncthreads();
   }
 }
 
-// One output tile of a gradient product: workgroup `bid` of the `nwg` the product
-// was given (kRole 0 runs only the tiles holding live rows and lets the rest go).
-template <typename T, int kRole, typename O>
-__device__ __forceinline__ void product_tile(const ProductArgs& a, int bid, int nwg, int tiles_m,
-                                             int tiles_n, char* lds) {
+// One dH tile: workgroup `bid` of the launch's first ones, over the M tiles that
+// hold live rows (the rest let go).  C[m = live row r][n = d] goes to
+// out[out_rows[m] * ld_out + n].
+template <typename T, typename O>
+__device__ __forceinline__ void dh_tile(const ProductArgs& a, int bid, int tiles_m, int tiles_n,
+                                        char* lds) {
   const int64_t na = *a.live;
-  int nk = a.nk;
   int64_t m_limit = a.m_limit;
-  if (kRole == 0) {
-    const int live_m = (int)ceil_div(na, kTile);
-    if (live_m < tiles_m) tiles_m = live_m;
-    nwg = tiles_m * tiles_n;
-    if (bid >= nwg) return;
-    if (na < m_limit) m_limit = na;
-  } else {
-    const int live_k = (int)ceil_div(na * (int64_t)sizeof(T), kStageBytes);
-    if (live_k < nk) nk = live_k;
-  }
+  const int live_m = (int)ceil_div(na, kTile);
+  if (live_m < tiles_m) tiles_m = live_m;
+  const int nwg = tiles_m * tiles_n;
+  if (bid >= nwg) return;
+  if (na < m_limit) m_limit = na;
   int tm, tn;
   tile_coords(bid, nwg, tiles_m, tiles_n, a.group_m, tm, tn);
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
   f32x4 acc[kBI][kBJ];
   zero_acc(acc);
-  gemm_tile<T, false, true>(a.A, a.B, m0, n0, nk, (lds_t*)lds, acc);
+  gemm_tile<T, false, true>(a.A, a.B, m0, n0, a.nk, (lds_t*)lds, acc);
 
-  if (kRole == 1) {
-    store_dw_tile<O>(acc, lds, (O*)a.out, a.ld_out, n0, m0, a.n_limit, m_limit, a.zero_from,
-                     a.accumulate);
-    return;
-  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / kWN, wn = wave % kWN;
   const int64_t mbase = m0 + wm * (kTile / kWM) + (lane >> 4) * 4;
@@ -431,23 +467,126 @@ __device__ __forceinline__ void product_tile(const ProductArgs& a, int bid, int 
   }
 }
 
+// The next dW tile for a workgroup on XCD `xcd`: a logical id from that XCD's own
+// run (the runs tile_coords gives the XCDs) while it lasts, then from the other
+// XCDs' runs in turn, as (M tile, N tile), or tm = -1 once every run is handed
+// out.  queue[x] counts the ids handed out of XCD x's run; the row compaction
+// clears it before each launch.  Taking from another XCD's run balances XCDs that
+// finish their own at different times (their clocks differ by a few percent).
+// Called by one thread; the tile counts pass through an empty asm statement so
+// that the divisions are not hoisted out of the caller's tile loop, where their
+// precomputed reciprocals would stay live across the K loop.
+__device__ __forceinline__ void grab_tile(int32_t* queue, int xcd, int tiles_m, int tiles_n,
+                                          int group_m, int& tm, int& tn) {
+  __asm__("" : "+s"(tiles_m), "+s"(tiles_n), "+s"(group_m));
+  const int total = tiles_m * tiles_n;
+  for (int k = 0; k < 8; ++k) {
+    const int x = (xcd + k) & 7;
+    int start, len;
+    xcd_run(x, total, start, len);
+    const int t = __hip_atomic_fetch_add(queue + x, 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    if (t < len) {
+      logical_coords(start + t, tiles_m, tiles_n, group_m, tm, tn);
+      return;
+    }
+  }
+  tm = -1;
+  tn = 0;
+}
+
+// The dW tiles, C[m = d][n = v] = sum over the live rows r of HT[d][r] dz[r][v],
+// stored as out[n * ld_out + m]: each of a fixed number of workgroups takes tiles
+// from the queues until none is left, with the K pipeline running on from one
+// tile into the next (gemm_tile_chain_split), so a tile's epilogue overlaps the next
+// tile's first loads.
+// The K loop runs over the stages covering the live rows, rounded up to an even
+// count (the rows past the live count up to the next 256 are zero in both
+// operands).
+//
+// Thread 0 takes each tile three tiles ahead, during the current tile's epilogue,
+// and puts its coordinates in a ring of four LDS slots at the epilogue's end; the
+// other waves read them after the next tile's K-loop barriers, so no tile waits
+// on a queue access or on an extra barrier.  Every workgroup stops after the
+// first empty slot, having issued the same barriers in every wave.
+template <typename T, typename O>
+__device__ __forceinline__ void dw_tiles(const ProductArgs& a, int32_t* queue, int tiles_m,
+                                         int tiles_n, char* lds) {
+  const int xcd = (int)blockIdx.x & 7;
+  const int wave = threadIdx.x >> 6;
+  int32_t* ring_m = (int32_t*)(lds + kGemmLds + kDwEpiLds);
+  int32_t* ring_n = ring_m + 4;
+  lds_t* slice = (lds_t*)(lds + kGemmLds + wave * kDwSlice);
+  const int64_t na = *a.live;
+
+  if (na == 0) {
+    // no live row: every tile is zeros (added to out when accumulating)
+    f32x4 acc[kBI][kBJ];
+    zero_acc(acc);
+    for (;;) {
+      if (threadIdx.x == 0) grab_tile(queue, xcd, tiles_m, tiles_n, a.group_m, ring_m[0], ring_n[0]);
+      __syncthreads();
+      const int tm = ring_m[0], tn = ring_n[0];
+      __syncthreads();
+      if (tm < 0) return;
+      store_dw_tile_wave<O>(acc, slice, (O*)a.out, a.ld_out, (int64_t)tn * kTile,
+                            (int64_t)tm * kTile, a.n_limit, a.m_limit, a.zero_from,
+                            a.accumulate);
+    }
+  }
+  int nk = (int)ceil_div(na * (int64_t)sizeof(T), kStageBytes);
+  if (nk > a.nk) nk = a.nk;
+  nk += nk & 1;   // a.nk is even (the rows are padded to 256)
+
+  if (threadIdx.x == 0)
+    for (int q = 0; q < 3; ++q) grab_tile(queue, xcd, tiles_m, tiles_n, a.group_m, ring_m[q], ring_n[q]);
+  __syncthreads();
+  int tm = ring_m[0], tn = ring_n[0];
+  int tmn = ring_m[1], tnn = ring_n[1];
+  if (tm < 0) return;
+  i32x4 fa0[kBI], fb0[kBJ];
+  for (int k = 0;; ++k) {
+    const bool has_next = tmn >= 0;
+    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+    f32x4 acc[kBI][kBJ];
+    zero_acc(acc);
+    gemm_tile_chain_split<T>(a.A, a.B, m0, n0, has_next, (int64_t)tmn * kTile,
+                             (int64_t)tnn * kTile, nk, k == 0, (lds_t*)lds, acc, fa0, fb0);
+    // (taken before the epilogue's stores, so waiting for it waits for nothing that
+    // the next tile's first K stage does not wait for anyway)
+    int am = -1, an = 0;
+    if (threadIdx.x == 0) grab_tile(queue, xcd, tiles_m, tiles_n, a.group_m, am, an);
+    store_dw_tile_wave<O>(acc, slice, (O*)a.out, a.ld_out, n0, m0, a.n_limit, a.m_limit,
+                          a.zero_from, a.accumulate);
+    if (threadIdx.x == 0) {
+      ring_m[(k + 3) & 3] = am;
+      ring_n[(k + 3) & 3] = an;
+    }
+    if (!has_next) break;
+    tm = tmn;
+    tn = tnn;
+    tmn = ring_m[(k + 2) & 3];
+    tnn = ring_n[(k + 2) & 3];
+  }
+}
+
 // dH and dW in one launch.  Workgroups [0, dh_slots) take dH tiles (long: K runs
-// over the vocabulary), the rest dW tiles (short: K runs over the live rows).  The
-// dH tiles are dispatched first, and the dW tiles fill the CUs that the last
-// partial round of dH tiles leaves idle.  dh_slots is a multiple of 8, so a dW
-// workgroup's XCD is still its index modulo 8.
+// over the vocabulary), one each; the rest (one per compute unit) take the dW
+// tiles (short: K runs over the live rows) from the queues.  The dH workgroups
+// are dispatched first, and the dW workgroups start on the compute units that the
+// last partial round of dH tiles leaves idle, the others as the dH tiles finish.
+// dh_slots is a multiple of 8, so a dW workgroup's XCD is still its index modulo 8.
 template <typename T, typename O>
 __global__ __launch_bounds__(kThreads) void grad_products_kernel(ProductArgs dh, ProductArgs dw,
-                                                                 int dh_slots, int dh_tiles_m,
-                                                                 int dh_tiles_n, int dw_tiles_m,
-                                                                 int dw_tiles_n) {
-  __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+                                                                 int32_t* queue, int dh_slots,
+                                                                 int dh_tiles_m, int dh_tiles_n,
+                                                                 int dw_tiles_m, int dw_tiles_n) {
+  __shared__ __attribute__((aligned(16))) char lds[kGradLds];
   const int bid = (int)blockIdx.x;
   if (bid < dh_slots)
-    product_tile<T, 0, O>(dh, bid, dh_tiles_m * dh_tiles_n, dh_tiles_m, dh_tiles_n, lds);
+    dh_tile<T, O>(dh, bid, dh_tiles_m, dh_tiles_n, lds);
   else
-    product_tile<T, 1, O>(dw, bid - dh_slots, (int)gridDim.x - dh_slots, dw_tiles_m, dw_tiles_n,
-                          lds);
+    dw_tiles<T, O>(dw, queue, dw_tiles_m, dw_tiles_n, lds);
 }
 
 // The chunk's live H rows, Hg[r][d] = H[rows[r]][d], and their transpose
@@ -565,8 +704,10 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     // beyond that a scan kernel forms the block offsets first
     int32_t* bbase = nb > 64 ? bcnt + nb : nullptr;
     int32_t* ytg = (int32_t*)(a.ws + L.ytg);
+    int32_t* dwq = (int32_t*)(a.ws + L.dwq);
     const CompactArgs ca{a.y + c0, cmask, a.ignore_index, a.coef + c0, a.lse + c0, a.grad_output,
-                         a.inv_tau, nc, ncp, bcnt, live, rows, rowpos, gl, bbase, a.v_real, ytg};
+                         a.inv_tau, nc, ncp, bcnt, live, rows, rowpos, gl, bbase, a.v_real, ytg,
+                         dwq};
     hipLaunchKernelGGL(live_count_kernel, dim3(nb), dim3(kCompactBlock), 0, s, ca);
     if (bbase)
       hipLaunchKernelGGL(block_scan_kernel, dim3(1), dim3(kCompactBlock), 0, s,
@@ -600,8 +741,12 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
                    a.accumulate_dw ? a.v_real : (a.v_rows < VK ? a.v_rows : VK), a.v_real,
                    (c0 > 0 || a.accumulate_dw) ? 1 : 0, a.group_dw, live, nullptr};
     const int dh_slots = (int)ceil_div((int64_t)tiles_t * tiles_d, 8) * 8;
-    hipLaunchKernelGGL((grad_products_kernel<T, O>), dim3(dh_slots + tiles_d * tiles_v),
-                       dim3(kThreads), 0, s, ph, pw, dh_slots, tiles_t, tiles_d, tiles_d, tiles_v);
+    const int dw_tiles = tiles_d * tiles_v;
+    int dw_wgs = chain_workgroups();
+    if (dw_wgs < 8) dw_wgs = 8;
+    if (dw_wgs > dw_tiles) dw_wgs = (int)ceil_div(dw_tiles, 8) * 8;
+    hipLaunchKernelGGL((grad_products_kernel<T, O>), dim3(dh_slots + dw_wgs), dim3(kThreads), 0,
+                       s, ph, pw, dwq, dh_slots, tiles_t, tiles_d, tiles_d, tiles_v);
     ev.mark(7, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

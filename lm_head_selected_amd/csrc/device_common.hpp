@@ -15,6 +15,7 @@ typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -259,21 +259,6 @@ __global__ __launch_bounds__(kMergeTokens * kMergeRuns) void merge_kernel(MergeA
   a.logp[t] = lp;
 }
 
-// Workgroups of the chained forward: one per compute unit of the current device
-// (a multiple of 8), looked up once per device.
-static int chain_workgroups() {
-  static int cached[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    cached[dev] = cus / 8 * 8;
-  }
-  return cached[dev];
-}
-
 template <typename T>
 static void launch_tiles(const FwdTileArgs& a, int tiles_m, int tiles_n,
                          const StageEvents& ev, hipStream_t s) {

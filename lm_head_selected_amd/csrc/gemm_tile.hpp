@@ -152,6 +152,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(const Operand& op,
                    __builtin_amdgcn_readfirstlane(rec));
 }
 
+// Byte stride between consecutive K stages of an operand whose stages are evenly
+// spaced: an MN-contiguous operand, or a K-contiguous one stored row-major (no
+// grouping of stages).  The chained tile core takes only such operands.
+template <typename T>
+__device__ __forceinline__ int64_t stage_stride(const Operand& op, bool mn) {
+  return mn ? (int64_t)(kStageBytes / (int)sizeof(T)) * op.ld : (int64_t)kStageBytes;
+}
+
+// Buffer resource over `limit` bytes from `base` (none if limit <= 0; at most
+// 4 GB - 1), with wave-uniform fields kept in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const char* base, int64_t limit) {
+  const int32_t hi = (int32_t)(limit >> 32);
+  const uint32_t lo = (uint32_t)limit;
+  const uint32_t rec = hi < 0 ? 0u : (hi > 0 ? 0xffffffffu : lo);
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return make_rsrc((const void*)(uintptr_t)(((uint64_t)bhi << 32) | blo),
+                   __builtin_amdgcn_readfirstlane(rec));
+}
+
 // Direct-to-LDS load of 16 bytes per lane: lane l's bytes at voffset + soffset of
 // the resource land at LDS byte lds_addr + 16 l.  Issued as inline assembly so
 // that the compiler does not treat the in-flight LDS writes as aliasing every
@@ -166,6 +187,40 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voffset
                    :
                    : "v"(voffset), "s"(r), "s"(soffset), "s"(lds_addr)
                    : "memory", "m0");
+}
+// One wave's share of a stage of one operand under the split issue: kLoads pairs of
+// loads (lane offsets o0 and o1, the pair's K rows i * step further on), filling
+// the 1 KB LDS blocks lds_addr, + 4 KB, + 8 KB, ... in turn.  One asm block that
+// steps M0 and the scalar offset itself, so the eight destinations take no
+// registers of their own.  (s_nop after each M0 write: the wait state an M0 write
+// needs before an LDS-DMA load.)
+__device__ __forceinline__ void dma16_split(__amdgpu_buffer_rsrc_t r, uint32_t o0, uint32_t o1,
+                                            uint32_t step, uint32_t lds_addr) {
+  static_assert(kLoads == 4, "four pairs of loads per wave and stage");
+  uint32_t t;
+  __asm__ volatile(
+      "s_mov_b32 m0, %[l]\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v0], %[r], 0 offen lds\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v1], %[r], 0 offen lds\n\t"
+      "s_mov_b32 %[t], %[st]\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v0], %[r], %[t] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v1], %[r], %[t] offen lds\n\t"
+      "s_add_u32 %[t], %[t], %[st]\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v0], %[r], %[t] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v1], %[r], %[t] offen lds\n\t"
+      "s_add_u32 %[t], %[t], %[st]\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v0], %[r], %[t] offen lds\n\t"
+      "s_add_u32 m0, m0, 0x1000\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %[v1], %[r], %[t] offen lds"
+      : [t] "=&s"(t)
+      : [v0] "v"(o0), [v1] "v"(o1), [r] "s"(r), [st] "s"(step), [l] "s"(lds_addr)
+      : "memory", "m0", "scc");
 }
 #pragma clang diagnostic pop
 
@@ -524,6 +579,119 @@ __device__ __forceinline__ void gemm_tile_chain(const Operand& A, const Operand&
     for (int j = 0; j < kBJ; ++j) fb0[j] = read_frag<T, false>(s + kOpLds, rB + 16 * j, 0, lane);
     __builtin_amdgcn_sched_barrier(0);
   }
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) quarter(fa0, fb0, fa1, fb1, kt, 1, c);
+    wait_vm<0>();
+    pipe_barrier();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      quarter(fa1, fb1, fa0, fb0, kt + 1, 0, c);
+      if (c == 0) {
+        issue(kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  if (!has_next) {
+    wait_vm<0>();
+    pipe_barrier();
+  }
+}
+
+// gemm_tile_chain for a K-contiguous A stored row-major and an MN-contiguous B (the
+// dW product), with the loads split as gemm_tile splits them for these operands:
+// waves 0-3 load B, waves 4-7 A.  Each wave's operand is a plain stream of stages
+// at a fixed byte stride, selected once, and its eight loads of a stage go out
+// as one asm block, which keeps the scalar registers the loop needs within the
+// file (with the generic stage addressing of gemm_tile the compiler spilled
+// registers in the loop).  The first wait of a chained call also waits for the
+// caller's epilogue stores, which were issued after the next tile's stage-1 loads:
+// letting them stay in flight there, with a second wait count for the first stage,
+// likewise made the compiler spill.
+template <typename T>
+__device__ __forceinline__ void gemm_tile_chain_split(const Operand& A, const Operand& B,
+                                                      int64_t m0, int64_t n0, bool has_next,
+                                                      int64_t m0n, int64_t n0n, int nk,
+                                                      bool first, lds_t* lds,
+                                                      f32x4 (&acc)[kBI][kBJ],
+                                                      i32x4 (&fa0)[kBI], i32x4 (&fb0)[kBJ]) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / kWN, wn = wave % kWN;
+
+  const TileRange ta = tile_range(A, m0), tb = tile_range(B, n0);
+  const TileRange tan = tile_range(A, has_next ? m0n : m0);
+  const TileRange tbn = tile_range(B, has_next ? n0n : n0);
+  const int rA = wm * (kTile / kWM), rB = wn * (kTile / kWN);
+  const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
+
+  // stages nk and nk + 1 come from the next tile when there is one; waves 0-3 load
+  // B, waves 4-7 A, each the shares of waves lw and lw + 4
+  constexpr int kHalf = kWaves / 2;
+  const int lw = wave & (kHalf - 1);
+  const bool firstw = wave < kHalf;
+  uint32_t stepA, stepB;
+  const uint32_t offA0 = load_offset<T>(A, lw, lane, stepA);
+  const uint32_t offA1 = load_offset<T>(A, lw + kHalf, lane, stepA);
+  const uint32_t offB0 = load_offset<T>(B, lw, lane, stepB);
+  const uint32_t offB1 = load_offset<T>(B, lw + kHalf, lane, stepB);
+  // the one operand this wave loads, as a stream of stages at a fixed byte stride
+  const int64_t sstride = firstw ? stage_stride<T>(B, true) : stage_stride<T>(A, false);
+  const char* sbase = firstw ? tb.base : ta.base;
+  const char* sbase_n = firstw ? tbn.base : tan.base;
+  const int64_t slimit = firstw ? tb.limit : ta.limit;
+  const int64_t slimit_n = firstw ? tbn.limit : tan.limit;
+  const uint32_t so0 = firstw ? offB0 : offA0, so1 = firstw ? offB1 : offA1;
+  const uint32_t sstep = firstw ? stepB : stepA;
+  const uint32_t sregion = firstw ? (uint32_t)kOpLds : 0u;
+  auto issue = [&](int stage) {
+    const uint32_t s0 = lds_base + (stage & 1) * kStageLds + lw * 1024;
+    const bool nxt = has_next && stage >= nk;
+    const int ks = nxt ? stage - nk : stage;
+    const int64_t o = (int64_t)ks * sstride;
+    const __amdgpu_buffer_rsrc_t r =
+        range_rsrc((nxt ? sbase_n : sbase) + o, (nxt ? slimit_n : slimit) - o);
+    dma16_split(r, so0, so1, sstep, __builtin_amdgcn_readfirstlane(s0 + sregion));
+  };
+  auto quarter = [&](const i32x4 (&ca)[kBI], const i32x4 (&cb)[kBJ], i32x4 (&na)[kBI],
+                     i32x4 (&nb)[kBJ], int rstage, int rks, int c) {
+    const lds_t* s = lds + (rstage & 1) * kStageLds;
+    if (c == 0) {
+#pragma unroll
+      for (int j = 0; j < kBJ; ++j) nb[j] = read_frag<T, true>(s + kOpLds, rB + 16 * j, rks, lane);
+    }
+    na[2 * c] = read_frag<T, false>(s, rA + 16 * (2 * c), rks, lane);
+    na[2 * c + 1] = read_frag<T, false>(s, rA + 16 * (2 * c + 1), rks, lane);
+#pragma unroll
+    for (int i = 2 * c; i < 2 * c + 2; ++i)
+#pragma unroll
+      for (int j = 0; j < kBJ; ++j) Mma<T>::run(acc[i][j], ca[i], cb[j]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  i32x4 fa1[kBI], fb1[kBJ];
+  if (first) {
+    issue(0);
+    issue(1);
+    wait_vm<2 * kLoads>();   // stage 0 landed; stage 1 may be in flight
+    pipe_barrier();
+    const lds_t* s = lds;
+#pragma unroll
+    for (int i = 0; i < kBI; ++i) fa0[i] = read_frag<T, false>(s, rA + 16 * i, 0, lane);
+#pragma unroll
+    for (int j = 0; j < kBJ; ++j) fb0[j] = read_frag<T, true>(s + kOpLds, rB + 16 * j, 0, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // The MN operand's fragment reads outnumber the compiler's LDS wait counter (see
+  // gemm_tile): enter the loop with none in flight.
+  lgkm_drain();
   for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) quarter(fa0, fb0, fa1, fb1, kt, 1, c);

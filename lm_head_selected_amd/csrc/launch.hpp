@@ -26,11 +26,28 @@ struct WsLayout {
   // token indices, every token's compact row (-1 if dead), the gathered H rows and
   // each compact row's target id
   size_t bcnt = 0, live = 0, rows = 0, rowpos = 0, hg = 0, ytg = 0;
+  // the dW tile queues of the gradient launch: one counter per XCD
+  size_t dwq = 0;
   size_t bwd_bytes = 0;
   int64_t n_vt = 0;        // vocabulary tiles covering [0, v_real)
   int64_t v_k = 0;         // n_vt * 256: vocabulary extent of the dlogits buffer
   int64_t chunk = 0;       // tokens per backward chunk (multiple of 256)
 };
+
+// Workgroups of the persistent matrix-core launches: one per compute unit of the
+// current device (a multiple of 8), looked up once per device; 0 if unknown.
+inline int chain_workgroups() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = cus / 8 * 8;
+  }
+  return cached[dev];
+}
 
 // Validation flags (bit set in the flags word)
 enum : uint32_t { kFlagTarget = 1u, kFlagNonfinite = 2u, kFlagSid = 4u };
