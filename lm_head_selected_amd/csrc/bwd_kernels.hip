@@ -467,34 +467,6 @@ __device__ __forceinline__ void dh_tile(const ProductArgs& a, int bid, int tiles
   }
 }
 
-// The next dW tile for a workgroup on XCD `xcd`: a logical id from that XCD's own
-// run (the runs tile_coords gives the XCDs) while it lasts, then from the other
-// XCDs' runs in turn, as (M tile, N tile), or tm = -1 once every run is handed
-// out.  queue[x] counts the ids handed out of XCD x's run; the row compaction
-// clears it before each launch.  Taking from another XCD's run balances XCDs that
-// finish their own at different times (their clocks differ by a few percent).
-// Called by one thread; the tile counts pass through an empty asm statement so
-// that the divisions are not hoisted out of the caller's tile loop, where their
-// precomputed reciprocals would stay live across the K loop.
-__device__ __forceinline__ void grab_tile(int32_t* queue, int xcd, int tiles_m, int tiles_n,
-                                          int group_m, int& tm, int& tn) {
-  __asm__("" : "+s"(tiles_m), "+s"(tiles_n), "+s"(group_m));
-  const int total = tiles_m * tiles_n;
-  for (int k = 0; k < 8; ++k) {
-    const int x = (xcd + k) & 7;
-    int start, len;
-    xcd_run(x, total, start, len);
-    const int t = __hip_atomic_fetch_add(queue + x, 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    if (t < len) {
-      logical_coords(start + t, tiles_m, tiles_n, group_m, tm, tn);
-      return;
-    }
-  }
-  tm = -1;
-  tn = 0;
-}
-
 // The dW tiles, C[m = d][n = v] = sum over the live rows r of HT[d][r] dz[r][v],
 // stored as out[n * ld_out + m]: each of a fixed number of workgroups takes tiles
 // from the queues until none is left, with the K pipeline running on from one

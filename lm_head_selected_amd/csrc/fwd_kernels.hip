@@ -114,46 +114,92 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int t
   tile_partials<false>(acc, a, tm, v0, t0, (float2(*)[kTile])lds);
 }
 
-// A fixed number of workgroups (a multiple of 8), each computing a sequence of
-// logit tiles with the K pipeline running on from one tile into the next
-// (gemm_tile_chain), so a tile's epilogue overlaps the next tile's first loads.
-// Workgroup b sits on XCD b % 8 and walks that XCD's run of logical tile ids (the
-// runs tile_coords gives the XCDs), strided by the number of workgroups per XCD:
-// the tiles resident together on an XCD are the same as with one workgroup per
-// tile.  Needs an even number of K stages.
-template <typename T>
+// A fixed number of workgroups (one per compute unit, a multiple of 8), each
+// computing a sequence of logit tiles with the K pipeline running on from one
+// tile into the next (gemm_tile_chain), so a tile's epilogue overlaps the next
+// tile's first loads.  Workgroup b sits on XCD b % 8 and works through that XCD's
+// run of logical tile ids (the runs tile_coords gives the XCDs), so the tiles
+// resident together on an XCD are the same as with one workgroup per tile.
+// kQueue: the workgroups take the ids from per-XCD queues (grab_tile), and an XCD
+// that empties its run takes ids from the others' runs, which balances XCDs that
+// run at different clocks (a few percent apart); thread 0 takes each id three
+// tiles ahead and passes it on through a ring of four LDS slots, as the dW tiles
+// of the backward do.  Without kQueue (no queue memory: the vocabulary-shard
+// entry) workgroup b takes every (per-XCD count)-th id of its run from b / 8 on.
+// Needs an even number of K stages.
+template <typename T, bool kQueue>
 __global__ __launch_bounds__(kThreads) void fwd_tile_chain_kernel(FwdTileArgs a, int tiles_m,
-                                                                  int tiles_n) {
-  // pipeline buffers, then the per-half row statistics (one LDS object: see above)
-  __shared__ __attribute__((aligned(16))) char lds[kGemmLds + 2 * kTile * sizeof(float2)];
-  const int per_xcd = (int)gridDim.x >> 3;
-  int start, len;
-  xcd_run((int)blockIdx.x & 7, tiles_m * tiles_n, start, len);
-  int id = (int)blockIdx.x >> 3;
-  if (id >= len) return;
+                                                                  int tiles_n, int32_t* queue) {
+  // pipeline buffers, then the per-half row statistics, then the ring of queued
+  // tiles (one LDS object: see above)
+  constexpr int kStats = 2 * kTile * (int)sizeof(float2);
+  __shared__ __attribute__((aligned(16))) char lds[kGemmLds + kStats + (kQueue ? 32 : 0)];
   const int64_t esz = Elem<T>::size;
   const int nk = (int)(a.d_model * esz / kStageBytes);
   const Operand A = nt_row_major(a.W, a.d_model * esz, a.v_real);
   const Operand B = nt_row_major(a.H, a.d_model * esz, a.n_tokens);
   float2(*half_stats)[kTile] = (float2(*)[kTile])(lds + kGemmLds);
   i32x4 fa0[kBI], fb0[kBJ];
-  int tm, tn;
-  logical_coords(start + id, tiles_m, tiles_n, a.group_m, tm, tn);
-  for (bool first = true; id < len; first = false) {
-    const int nid = id + per_xcd;
-    const bool has_next = nid < len;
-    int tmn = tm, tnn = tn;
-    if (has_next) logical_coords(start + nid, tiles_m, tiles_n, a.group_m, tmn, tnn);
-    const int64_t v0 = (int64_t)tm * kTile, t0 = (int64_t)tn * kTile;
-    f32x4 acc[kBI][kBJ];
-    zero_acc(acc);
-    gemm_tile_chain<T>(A, B, v0, t0, has_next, (int64_t)tmn * kTile, (int64_t)tnn * kTile, nk,
-                       first, (lds_t*)lds, acc, fa0, fb0);
-    tile_partials<true>(acc, a, tm, v0, t0, half_stats);
-    id = nid;
-    tm = tmn;
-    tn = tnn;
+  if constexpr (kQueue) {
+    const int xcd = (int)blockIdx.x & 7;
+    int32_t* ring_m = (int32_t*)(lds + kGemmLds + kStats);
+    int32_t* ring_n = ring_m + 4;
+    if (threadIdx.x == 0)
+      for (int q = 0; q < 3; ++q)
+        grab_tile(queue, xcd, tiles_m, tiles_n, a.group_m, ring_m[q], ring_n[q]);
+    __syncthreads();
+    int tm = ring_m[0], tn = ring_n[0];
+    int tmn = ring_m[1], tnn = ring_n[1];
+    if (tm < 0) return;
+    for (int k = 0;; ++k) {
+      const bool has_next = tmn >= 0;
+      const int64_t v0 = (int64_t)tm * kTile, t0 = (int64_t)tn * kTile;
+      f32x4 acc[kBI][kBJ];
+      zero_acc(acc);
+      gemm_tile_chain<T>(A, B, v0, t0, has_next, (int64_t)tmn * kTile, (int64_t)tnn * kTile,
+                         nk, k == 0, (lds_t*)lds, acc, fa0, fb0);
+      int am = -1, an = 0;
+      if (threadIdx.x == 0) grab_tile(queue, xcd, tiles_m, tiles_n, a.group_m, am, an);
+      tile_partials<true>(acc, a, tm, v0, t0, half_stats);
+      if (threadIdx.x == 0) {
+        ring_m[(k + 3) & 3] = am;
+        ring_n[(k + 3) & 3] = an;
+      }
+      if (!has_next) break;
+      tm = tmn;
+      tn = tnn;
+      tmn = ring_m[(k + 2) & 3];
+      tnn = ring_n[(k + 2) & 3];
+    }
+  } else {
+    const int per_xcd = (int)gridDim.x >> 3;
+    int start, len;
+    xcd_run((int)blockIdx.x & 7, tiles_m * tiles_n, start, len);
+    int id = (int)blockIdx.x >> 3;
+    if (id >= len) return;
+    int tm, tn;
+    logical_coords(start + id, tiles_m, tiles_n, a.group_m, tm, tn);
+    for (bool first = true; id < len; first = false) {
+      const int nid = id + per_xcd;
+      const bool has_next = nid < len;
+      int tmn = tm, tnn = tn;
+      if (has_next) logical_coords(start + nid, tiles_m, tiles_n, a.group_m, tmn, tnn);
+      const int64_t v0 = (int64_t)tm * kTile, t0 = (int64_t)tn * kTile;
+      f32x4 acc[kBI][kBJ];
+      zero_acc(acc);
+      gemm_tile_chain<T>(A, B, v0, t0, has_next, (int64_t)tmn * kTile, (int64_t)tnn * kTile,
+                         nk, first, (lds_t*)lds, acc, fa0, fb0);
+      tile_partials<true>(acc, a, tm, v0, t0, half_stats);
+      id = nid;
+      tm = tmn;
+      tn = tnn;
+    }
   }
+}
+
+// Clears the tile queues of a persistent launch (8 counters).
+__global__ void clear_queue_kernel(int32_t* queue) {
+  if (threadIdx.x < 8) queue[threadIdx.x] = 0;
 }
 
 // One wave per token: z[t, y_t] * inv_tau = inv_tau * sum_d H[t, d] W[y_t, d] for
@@ -260,15 +306,20 @@ __global__ __launch_bounds__(kMergeTokens * kMergeRuns) void merge_kernel(MergeA
 }
 
 template <typename T>
-static void launch_tiles(const FwdTileArgs& a, int tiles_m, int tiles_n,
+static void launch_tiles(const FwdTileArgs& a, int tiles_m, int tiles_n, int32_t* queue,
                          const StageEvents& ev, hipStream_t s) {
   const int64_t nk = a.d_model * (int64_t)sizeof(T) / kStageBytes;
   const int g = chain_workgroups();
   if (nk % 2 == 0 && g >= 8) {
     const int total = tiles_m * tiles_n;
     const int used = total < g ? (total + 7) / 8 * 8 : g;
-    hipLaunchKernelGGL(fwd_tile_chain_kernel<T>, dim3(used), dim3(kThreads), 0, s, a, tiles_m,
-                       tiles_n);
+    if (queue) {
+      hipLaunchKernelGGL((fwd_tile_chain_kernel<T, true>), dim3(used), dim3(kThreads), 0, s, a,
+                         tiles_m, tiles_n, queue);
+    } else {
+      hipLaunchKernelGGL((fwd_tile_chain_kernel<T, false>), dim3(used), dim3(kThreads), 0, s, a,
+                         tiles_m, tiles_n, queue);
+    }
   } else {
     hipLaunchKernelGGL(fwd_tile_kernel<T>, dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, a,
                        tiles_m, tiles_n);
@@ -276,13 +327,18 @@ static void launch_tiles(const FwdTileArgs& a, int tiles_m, int tiles_n,
   ev.mark(1, s);
 }
 
-hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt,
+hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt, int32_t* queue,
                             const StageEvents& ev, hipStream_t s) {
   const int tiles_m = (int)n_vt;
   const int tiles_n = (int)ceil_div(a.n_tokens, kTokenTile);
   if (tiles_m * tiles_n == 0) return hipSuccess;
-  if (dtype == 0) launch_tiles<__bf16>(a, tiles_m, tiles_n, ev, s);
-  else launch_tiles<float>(a, tiles_m, tiles_n, ev, s);
+  if (dtype == 0) launch_tiles<__bf16>(a, tiles_m, tiles_n, queue, ev, s);
+  else launch_tiles<float>(a, tiles_m, tiles_n, queue, ev, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear_queue(int32_t* queue, hipStream_t s) {
+  hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(64), 0, s, queue);
   return hipGetLastError();
 }
 

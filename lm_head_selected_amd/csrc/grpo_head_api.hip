@@ -127,6 +127,7 @@ gh::WsLayout layout(const grpo_head_params* p, bool with_gemm = true) {
   L.seq_G = take((size_t)S * 4);
   L.scal = take(64);
   L.flags = take(64);
+  L.fq = take(with_gemm ? 8 * 4 : 0);
   L.fwd_bytes = off;
   if (!with_gemm) return L;
 
@@ -189,11 +190,14 @@ int run_logp(const grpo_head_params* p, const gh::WsLayout& L, char* w, const vo
              const void* W, const int64_t* y, const uint8_t* mask, float* logp, float* lse,
              hipStream_t s) {
   if (p->n_tokens == 0) return GRPO_HEAD_OK;
+  int32_t* fq = (int32_t*)(w + L.fq);
+  hipError_t e = gh::launch_clear_queue(fq, s);
+  if (e != hipSuccess) return hip_fail(e, "queue clear kernel");
   g_marks.mark(0, s);
   gh::FwdTileArgs fa{W, H, p->n_tokens, p->d_model, p->v_real, p->inv_tau,
                      (float2*)(w + L.partials),
                      logit_group(p->n_tokens, p->d_model, p->dtype == GRPO_HEAD_F32 ? 4 : 2)};
-  hipError_t e = gh::launch_fwd_tiles(p->dtype, fa, L.n_vt, g_marks, s);
+  e = gh::launch_fwd_tiles(p->dtype, fa, L.n_vt, fq, g_marks, s);
   if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
   gh::TargetArgs ta{H, W, y, mask, p->n_tokens, p->d_model, p->v_real, p->ignore_index,
                     p->inv_tau, 0, (float*)(w + L.zy)};
@@ -345,7 +349,7 @@ int grpo_head_shard_partials(const grpo_head_params* p, int64_t v_begin, int64_t
   if (n_st > 0) {
     gh::FwdTileArgs fa{W_shard, H, p->n_tokens, p->d_model, rows, p->inv_tau, (float2*)partials,
                        logit_group(p->n_tokens, p->d_model, p->dtype == GRPO_HEAD_F32 ? 4 : 2)};
-    hipError_t e = gh::launch_fwd_tiles(p->dtype, fa, n_st, gh::StageEvents{}, s);
+    hipError_t e = gh::launch_fwd_tiles(p->dtype, fa, n_st, nullptr, gh::StageEvents{}, s);
     if (e != hipSuccess) return hip_fail(e, "forward tile kernel");
   }
   gh::TargetArgs ta{H, W_shard, y, mask, p->n_tokens, p->d_model, rows, p->ignore_index,

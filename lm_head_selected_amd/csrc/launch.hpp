@@ -19,6 +19,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct WsLayout {
   // forward / segment stage
   size_t partials = 0, zy = 0, seq_L = 0, seq_F = 0, seq_G = 0, scal = 0, flags = 0;
+  size_t fq = 0;           // the forward tile launch's queues: one counter per XCD
   size_t fwd_bytes = 0;
   // backward (reuses the workspace from offset 0)
   size_t bflags = 0, gl = 0, dz = 0, ht = 0;
@@ -115,9 +116,12 @@ struct BwdArgs {
   int grad_bf16;       // dH and dW are bf16 (else fp32)
 };
 
-// records stage event 1 after the tile launch
-hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt,
+// records stage event 1 after the tile launch; queue: the 8 tile-queue counters of
+// the chained launch, cleared beforehand by launch_clear_queue (null: a fixed
+// tile schedule)
+hipError_t launch_fwd_tiles(int dtype, const FwdTileArgs& a, int64_t n_vt, int32_t* queue,
                             const StageEvents& ev, hipStream_t s);
+hipError_t launch_clear_queue(int32_t* queue, hipStream_t s);
 hipError_t launch_target_logit(int dtype, const TargetArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_loss(const LossArgs& a, hipStream_t s);
