@@ -29,9 +29,11 @@
 // fragments of the MN-contiguous operand with the gfx950 transposing LDS read,
 // which delivers about half the bandwidth of a plain read, so each product keeps
 // exactly one such operand, on the side with the smaller per-wave fragment count.
-// dz is stored "v-tiled": [vocabulary / 256][chunk rows][256], so a 256x256
-// dlogits tile is one contiguous 128 KB block (bf16) and either product streams
-// it in large contiguous runs.
+// dz is stored "v-blocked": [vocabulary / 64][chunk rows][64], so a K stage of the
+// dH product (256 rows x 64 vocabulary entries, bf16) is one contiguous 32 KB run,
+// and a K stage of the dW product (64 rows x 256 entries) four runs of 8 KB.  (A
+// layout blocked by 256, whose dH stages are 256 runs of 128 B, 512 B apart,
+// measured 0.18 ms slower in the gradient launch.)
 #include <type_traits>
 
 #include "gemm_tile.hpp"
@@ -66,7 +68,7 @@ struct DlogitsArgs {
   int64_t chunk_tokens;           // rows of H and gl inside the chunk
   int64_t d_model, v_real;
   float inv_tau;
-  void* dz;                       // v-tiled [n_vt][dz_rows][256]
+  void* dz;                       // v-blocked [4 n_vt][dz_rows][64]
   int64_t dz_rows;
   int group_m;
   const int32_t* live;            // live row count (device); token tiles past it are skipped
@@ -228,9 +230,10 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
   const float c2 = a.inv_tau * kLog2e;
   // (g, lse2) of the lane's token columns; tokens past the chunk read zeros
   const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gl, (uint32_t)(a.chunk_tokens * 8));
-  // this tile's block of dz: rows t0 .. t0 + 255 of vocabulary group tm, one
-  // contiguous [256][256] block
-  char* tile = (char*)a.dz + vtiled_offset(t0, v0, a.dz_rows, esz);
+  // this tile's part of dz: rows t0 .. t0 + 255 of the 4 vocabulary blocks from
+  // v0 / 64, each row's 64 elements of a block one contiguous run
+  char* tile = (char*)a.dz + vblocked_offset(t0, v0, a.dz_rows, esz);
+  const int64_t block_bytes = a.dz_rows * 64 * esz;   // between 64-element blocks
   // bf16: the block is staged in LDS (now free) and written out as whole rows;
   // 32-byte segment s of LDS row t sits at segment s ^ (t & 15)
   char* L = lds;
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
   // target element, rel its row within the wave's 128 rows
   auto column = [&](int j, int tl, float g, float lse2, int32_t rel, bool own, auto fix) {
     constexpr bool kFix = decltype(fix)::value;
-    char* rowp = tile + (int64_t)tl * 256 * esz;
+    char* rowp = tile + (int64_t)tl * 64 * esz;
 #pragma unroll
     for (int i = 0; i < kBI; ++i) {
       float d[4];
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
         const int seg = (byte >> 5) ^ (tl & 15);
         *(i32x2*)(L + tl * 512 + seg * 32 + (byte & 31)) = __builtin_bit_cast(i32x2, q);
       } else {
-        Store4<T>::run(rowp + v * esz, d[0], d[1], d[2], d[3]);
+        Store4<T>::run(rowp + (v >> 6) * block_bytes + (v & 63) * esz, d[0], d[1], d[2], d[3]);
       }
     }
   };
@@ -283,14 +286,16 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
   }
   if (sizeof(T) == 2) {
     __syncthreads();
-    // 256 rows x 32 chunks of 16 B, row-major: one wave writes two whole rows
+    // 256 rows x 32 chunks of 16 B: one wave writes two whole rows, each as 4 runs
+    // of 128 B (chunks 8 b .. 8 b + 7 go to block b)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int idx = q * kThreads + threadIdx.x;
       const int t = idx >> 5, c = idx & 31;
       const int seg = (c >> 1) ^ (t & 15);
       const i32x4 v = *(const i32x4*)(L + t * 512 + seg * 32 + (c & 1) * 16);
-      __builtin_nontemporal_store(v, (i32x4*)(tile + (int64_t)t * 512 + c * 16));
+      __builtin_nontemporal_store(
+          v, (i32x4*)(tile + (c >> 3) * block_bytes + (int64_t)t * 128 + (c & 7) * 16));
     }
   }
 }
@@ -701,14 +706,14 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     // dH rows of the chunk: M = live row r (dz rows), N = d (W read MN-contiguous),
     // K = v; row r goes to token rows[r].  W rows >= v_real are never read (they
     // load as zeros).
-    ProductArgs ph{nt_vtiled(dz, R, esz, (int64_t)tiles_v * R * 256 * esz),
+    ProductArgs ph{nt_vblocked(dz, R, esz, (int64_t)tiles_v * R * 256 * esz),
                    mn_row_major(a.W, D * esz, a.v_real, D, esz), (int)(VK * esz / kStageBytes),
                    dH + c0 * D, D, nc, D, INT64_MAX, 0, a.group_dh, live, rows};
 
     // dW: M = d (HT K-contiguous), N = v (dz read MN-contiguous), K = live row.
     // Rows [v_real, VK) of the last tile are written as zeros, or, when
     // accumulating into the caller's dW, not written at all.
-    ProductArgs pw{nt_row_major(ht, R * esz, D), mn_vtiled(dz, R, esz, tiles_v),
+    ProductArgs pw{nt_row_major(ht, R * esz, D), mn_vblocked(dz, R, esz, 4 * tiles_v),
                    (int)(ncp * esz / kStageBytes), dW, D, D,
                    a.accumulate_dw ? a.v_real : (a.v_rows < VK ? a.v_rows : VK), a.v_real,
                    (c0 > 0 || a.accumulate_dw) ? 1 : 0, a.group_dw, live, nullptr};

@@ -63,14 +63,16 @@ constexpr int kLoads = kOpLds / 1024 / kWaves;  // wave-wide 1 KB loads per oper
 //   bytes from base_t; bytes beyond load as zeros.
 // NT: byte (row r of the tile, K byte kb) = r * ld + stage_off(kb / 128) + kb % 128,
 //     stage_off(s) = (s >> group_shift) * group_bytes + (s & (2^group_shift - 1)) * 128.
-// MN: byte (K row k, element r of the tile) = k * ld + r * element size.
+// MN: byte (K row k, element r of the tile) = k * ld + r * element size, or, with
+//     group_bytes > 0 (blocked by 64 elements), k * ld + (r / 64) * group_bytes +
+//     (r % 64) * element size.
 struct Operand {
   const char* base;
   int64_t ld;           // bytes between rows (NT: M/N rows; MN: K rows)
   int64_t tile_bytes;   // bytes between 256-wide M/N tiles
   int64_t span;         // valid bytes from base (see above)
   int64_t cap;          // most bytes one tile's resource may cover
-  int64_t group_bytes;  // NT: bytes between K-stage groups
+  int64_t group_bytes;  // NT: bytes between K-stage groups; MN: between 64-element blocks
   int32_t group_shift;  // NT: log2(stages per group)
   int32_t mn;           // 1: MN-contiguous
 };
@@ -80,13 +82,14 @@ struct Operand {
 __host__ __device__ inline Operand nt_row_major(const void* base, int64_t pitch, int64_t rows) {
   return Operand{(const char*)base, pitch, 256 * pitch, rows * pitch, 256 * pitch, 0, 30, 0};
 }
-// The v-tiled layout [groups][rows_pad][256 elements] (dz) read K-contiguous with
-// rows = its rows and K = the 256-element groups in order.
-__host__ __device__ inline Operand nt_vtiled(const void* base, int64_t rows_pad, int64_t esz,
-                                            int64_t total_bytes) {
-  const int32_t shift = esz == 2 ? 2 : 3;   // 128-byte stages per 256-element group
-  return Operand{(const char*)base, 256 * esz, 256 * 256 * esz, total_bytes, total_bytes,
-                 rows_pad * 256 * esz, shift, 0};
+// The v-blocked layout [blocks][rows_pad][64 elements] (dz) read K-contiguous with
+// rows = its rows and K = the 64-element blocks in order: a stage of 256 rows is
+// one contiguous run (bf16: one block; fp32: half a block per row).
+__host__ __device__ inline Operand nt_vblocked(const void* base, int64_t rows_pad, int64_t esz,
+                                              int64_t total_bytes) {
+  const int32_t shift = esz == 2 ? 0 : 1;   // 128-byte stages per 64-element block
+  return Operand{(const char*)base, 64 * esz, 256 * 64 * esz, total_bytes, total_bytes,
+                 rows_pad * 64 * esz, shift, 0};
 }
 // Row-major [k_rows][cols] (pitch bytes per row) read MN-contiguous, K = its rows:
 // K rows >= k_rows and columns >= cols of the last valid row load as zeros.
@@ -95,16 +98,17 @@ __host__ __device__ inline Operand mn_row_major(const void* base, int64_t pitch,
   return Operand{(const char*)base, pitch, 256 * esz,
                  k_rows > 0 ? (k_rows - 1) * pitch + cols * esz : 0, (int64_t)1 << 62, 0, 30, 1};
 }
-// The v-tiled layout read MN-contiguous: K = its rows, M/N = the elements.
-__host__ __device__ inline Operand mn_vtiled(const void* base, int64_t rows_pad, int64_t esz,
-                                            int64_t groups) {
-  const int64_t tb = rows_pad * 256 * esz;
-  return Operand{(const char*)base, 256 * esz, tb, groups * tb, tb, 0, 30, 1};
+// The v-blocked layout read MN-contiguous: K = its rows, M/N = the elements; a
+// 256-element tile is 4 blocks, and a K row of it 4 runs of 64 elements.
+__host__ __device__ inline Operand mn_vblocked(const void* base, int64_t rows_pad, int64_t esz,
+                                              int64_t blocks) {
+  const int64_t bb = rows_pad * 64 * esz;
+  return Operand{(const char*)base, 64 * esz, 4 * bb, blocks * bb, 4 * bb, bb, 30, 1};
 }
-// Byte offset of (row, element v) in the v-tiled layout.
-__host__ __device__ inline int64_t vtiled_offset(int64_t row, int64_t v, int64_t rows_pad,
-                                                 int64_t esz) {
-  return (v >> 8) * rows_pad * 256 * esz + row * 256 * esz + (v & 255) * esz;
+// Byte offset of (row, element v) in the v-blocked layout.
+__host__ __device__ inline int64_t vblocked_offset(int64_t row, int64_t v, int64_t rows_pad,
+                                                   int64_t esz) {
+  return (v >> 6) * rows_pad * 64 * esz + row * 64 * esz + (v & 63) * esz;
 }
 
 // Base and valid byte count of one M/N tile of an operand.
@@ -290,9 +294,12 @@ __device__ __forceinline__ int swz_mn(int k) { return (k & 3) | ((k >> 1) & 4); 
 // that belong at that physical place.  Load i covers rows (NT) or K-rows (MN)
 // 64 i, 16 i or 8 i further on, which leaves every swizzle unchanged, so one
 // offset serves all loads.
-template <typename T>
+template <typename T, int kBlocked = -1>
 __device__ __forceinline__ uint32_t load_offset(const Operand& op, int wave, int lane,
                                                 uint32_t& step) {
+  // kBlocked: 1 or 0 when the caller knows whether an MN operand is blocked, -1
+  // to look at op.group_bytes
+  const bool blocked = kBlocked < 0 ? op.group_bytes != 0 : kBlocked != 0;
   if (!op.mn) {
     const int r = wave * 8 + (lane >> 3);                          // 8 rows of 128 B
     const int c = (lane & 7) ^ swz_nt(r);
@@ -303,11 +310,14 @@ __device__ __forceinline__ uint32_t load_offset(const Operand& op, int wave, int
     const int pc = lane & 31;                                      // physical chunk
     const int c = (((pc >> 1) ^ swz_mn(k)) << 1) | (pc & 1);
     step = (uint32_t)(kWaves * 2 * op.ld);
-    return (uint32_t)(k * op.ld + c * 16);
+    // blocked: 16-byte chunk c is element 8 c of the tile, in block c / 8
+    return blocked ? (uint32_t)(k * op.ld + (c >> 3) * op.group_bytes + (c & 7) * 16)
+                   : (uint32_t)(k * op.ld + c * 16);
   } else {
     const int k = wave;                                            // 1 K-row of 1 KB
     step = (uint32_t)(kWaves * op.ld);
-    return (uint32_t)(k * op.ld + lane * 16);
+    return blocked ? (uint32_t)(k * op.ld + (lane >> 4) * op.group_bytes + (lane & 15) * 16)
+                   : (uint32_t)(k * op.ld + lane * 16);
   }
 }
 
@@ -343,7 +353,8 @@ __device__ __forceinline__ i32x4 read_frag(const lds_t* region, int r0, int ks, 
 constexpr int kIssueSolo = 1;    // waves 0-3 load both operands for all 8 waves
 constexpr int kIssueSplit = 2;   // waves 0-3 load all of B, waves 4-7 all of A
 
-// acc[i][j] += A(m0 + wave rows, :) . B(n0 + wave cols, :) over nk K stages.
+// acc[i][j] += A(m0 + wave rows, :) . B(n0 + wave cols, :) over nk K stages.  An
+// MN-contiguous B is row-major (not blocked).
 //
 // Stage s lives in LDS buffer s % 2, filled with direct-to-LDS buffer loads
 // issued by a subset of the waves (kIssue; the reason is at the issue code).  A
@@ -384,8 +395,8 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   uint32_t stepA, stepB;
   const uint32_t offA0 = load_offset<T>(A, lw, lane, stepA);
   const uint32_t offA1 = load_offset<T>(A, lw + kHalf, lane, stepA);
-  const uint32_t offB0 = load_offset<T>(B, lw, lane, stepB);
-  const uint32_t offB1 = load_offset<T>(B, lw + kHalf, lane, stepB);
+  const uint32_t offB0 = load_offset<T, 0>(B, lw, lane, stepB);
+  const uint32_t offB1 = load_offset<T, 0>(B, lw + kHalf, lane, stepB);
   auto issue = [&](int stage) {
     const uint32_t s0 = lds_base + (stage & 1) * kStageLds + lw * 1024;
     const uint32_t s1 = s0 + kHalf * 1024;
@@ -599,8 +610,8 @@ __device__ __forceinline__ void gemm_tile_chain(const Operand& A, const Operand&
   }
 }
 
-// gemm_tile_chain for a K-contiguous A stored row-major and an MN-contiguous B (the
-// dW product), with the loads split as gemm_tile splits them for these operands:
+// gemm_tile_chain for a K-contiguous A stored row-major and an MN-contiguous B
+// blocked by 64 elements (the dW product), with the loads split as gemm_tile splits them for these operands:
 // waves 0-3 load B, waves 4-7 A.  Each wave's operand is a plain stream of stages
 // at a fixed byte stride, selected once, and its eight loads of a stage go out
 // as one asm block, which keeps the scalar registers the loop needs within the
@@ -617,7 +628,10 @@ __device__ __forceinline__ void gemm_tile_chain_split(const Operand& A, const Op
                                                       f32x4 (&acc)[kBI][kBJ],
                                                       i32x4 (&fa0)[kBI], i32x4 (&fb0)[kBJ]) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  // (the lane index made opaque: the per-lane offsets below are then formed on each
+  // call rather than hoisted out of the caller's tile loop and kept across it)
+  int lane = tid & 63;
+  __asm__("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kWN, wn = wave % kWN;
 
@@ -635,8 +649,8 @@ __device__ __forceinline__ void gemm_tile_chain_split(const Operand& A, const Op
   uint32_t stepA, stepB;
   const uint32_t offA0 = load_offset<T>(A, lw, lane, stepA);
   const uint32_t offA1 = load_offset<T>(A, lw + kHalf, lane, stepA);
-  const uint32_t offB0 = load_offset<T>(B, lw, lane, stepB);
-  const uint32_t offB1 = load_offset<T>(B, lw + kHalf, lane, stepB);
+  const uint32_t offB0 = load_offset<T, 1>(B, lw, lane, stepB);
+  const uint32_t offB1 = load_offset<T, 1>(B, lw + kHalf, lane, stepB);
   // the one operand this wave loads, as a stream of stages at a fixed byte stride
   const int64_t sstride = firstw ? stage_stride<T>(B, true) : stage_stride<T>(A, false);
   const char* sbase = firstw ? tb.base : ta.base;

@@ -138,7 +138,7 @@ gh::WsLayout layout(const grpo_head_params* p, bool with_gemm = true) {
   off = 0;
   L.bflags = take(64);
   L.gl = take((size_t)chunk * 8);
-  L.dz = take((size_t)chunk * L.v_k * esz);   // dlogits of one chunk, v-tiled
+  L.dz = take((size_t)chunk * L.v_k * esz);   // dlogits of one chunk, v-blocked
   L.ht = take((size_t)D * chunk * esz);       // the chunk's live H rows transposed
   L.bcnt = take((size_t)gh::ceil_div(chunk, gh::kCompactBlock) * 8);   // counts, then offsets
   L.live = take(4);
