@@ -54,7 +54,9 @@
  *     call enqueues nothing.  The return value is a grpo_head_status; on a
  *     non-zero status grpo_head_last_error() describes it.
  *   - Results are bitwise identical from run to run for identical inputs: every
- *     reduction has a fixed order and no result depends on atomics.
+ *     reduction has a fixed order and no result depends on atomics (atomic
+ *     counters in the workspace only decide which workgroup computes a tile; each
+ *     tile is computed whole, in a fixed order).
  *   - Calls that share a workspace must not overlap in time.
  *
  * Layouts.  Row-major, no padding between rows.
@@ -166,12 +168,13 @@ typedef struct grpo_head_params {
 } grpo_head_params;
 
 /* Bytes of device workspace grpo_head_fwd needs (per-tile partials, target
- * logits, per-sequence totals).  0 if p is invalid. */
+ * logits, per-sequence totals, tile-queue counters).  0 if p is invalid. */
 size_t grpo_head_fwd_workspace_size(const grpo_head_params* p);
 
 /* Bytes of device workspace grpo_head_bwd needs (the bf16 or fp32 dlogits of one
  * token chunk over the 256-padded vocabulary, the chunk's gathered hidden states
- * as rows and transposed, and per-token scalars and row indices); also at
+ * as rows and transposed, per-token scalars and row indices, and tile-queue
+ * counters); also at
  * least grpo_head_fwd_workspace_size(p), so one buffer serves all calls.
  * 0 if p is invalid. */
 size_t grpo_head_workspace_size(const grpo_head_params* p);
