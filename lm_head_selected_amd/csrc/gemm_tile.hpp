@@ -726,32 +726,28 @@ __device__ __forceinline__ void gemm_tile_chain_split(const Operand& A, const Op
   }
 }
 
-// The next tile of a persistent launch for a workgroup on XCD `xcd`: a logical id
-// from that XCD's own run (the runs tile_coords gives the XCDs) while it lasts,
-// then from the other XCDs' runs in turn, as (M tile, N tile), or tm = -1 once
-// every run is handed out.  queue[x] counts the ids handed out of XCD x's run and
-// starts each launch at zero.  Taking from another XCD's run balances XCDs that
-// finish their own at different times (their clocks differ by a few percent).
+// The next tile of a persistent launch for a workgroup on XCD `xcd` (queue_next:
+// its own XCD's run of logical ids first, then the other XCDs'), as (M tile,
+// N tile), or tm = -1 once every run is handed out.  queue[x] counts the ids handed
+// out of XCD x's run and starts each launch at zero.  Taking from another XCD's
+// run balances XCDs that finish their own at different times (their clocks differ
+// by a few percent).
 // Called by one thread; the tile counts pass through an empty asm statement so
 // that the divisions are not hoisted out of the caller's tile loop, where their
 // precomputed reciprocals would stay live across the K loop.
 __device__ __forceinline__ void grab_tile(int32_t* queue, int xcd, int tiles_m, int tiles_n,
                                           int group_m, int& tm, int& tn) {
   __asm__("" : "+s"(tiles_m), "+s"(tiles_n), "+s"(group_m));
-  const int total = tiles_m * tiles_n;
-  for (int k = 0; k < 8; ++k) {
-    const int x = (xcd + k) & 7;
-    int start, len;
-    xcd_run(x, total, start, len);
-    const int t = __hip_atomic_fetch_add(queue + x, 1, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    if (t < len) {
-      logical_coords(start + t, tiles_m, tiles_n, group_m, tm, tn);
-      return;
-    }
+  auto take = [queue](int x) {
+    return __hip_atomic_fetch_add(queue + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  const int id = queue_next(take, xcd, tiles_m * tiles_n);
+  if (id < 0) {
+    tm = -1;
+    tn = 0;
+  } else {
+    logical_coords(id, tiles_m, tiles_n, group_m, tm, tn);
   }
-  tm = -1;
-  tn = 0;
 }
 
 // Set every accumulator whose wave-local M row (0..127) is >= vlim to -inf.

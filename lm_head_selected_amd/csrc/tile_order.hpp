@@ -47,4 +47,21 @@ GH_HOST_DEVICE inline void tile_coords(int bid, int nwg, int tiles_m, int tiles_
   logical_coords(xcd_logical(bid, nwg), tiles_m, tiles_n, group_m, tm, tn);
 }
 
+// The next tile of a persistent launch for a workgroup on XCD `xcd`: a logical id
+// from that XCD's own run while it lasts, then from the other XCDs' runs in turn
+// ((xcd + 1) & 7, ...), or -1 once every run is handed out.  take(x) returns the
+// number of ids handed out of XCD x's run so far and counts one more (on the device
+// an atomic add on a per-XCD counter that starts each launch at zero).
+template <typename Take>
+GH_HOST_DEVICE inline int queue_next(Take take, int xcd, int total) {
+  for (int k = 0; k < 8; ++k) {
+    const int x = (xcd + k) & 7;
+    int start, len;
+    xcd_run(x, total, start, len);
+    const int t = take(x);
+    if (t < len) return start + t;
+  }
+  return -1;
+}
+
 }  // namespace gh

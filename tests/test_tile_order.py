@@ -1,8 +1,10 @@
 """The matrix-core launches' tile order (csrc/tile_order.hpp) compiled on the host
 with g++: every workgroup-to-tile mapping is a bijection onto the tile grid, a
-launch of fewer workgroups covers exactly the first logical ids, and the chained
-forward's walk (a fixed number of workgroups, each taking every (nwg/8)-th id of
-its XCD's run) computes every tile exactly once."""
+launch of fewer workgroups covers exactly the first logical ids, the fixed chained
+walk (a fixed number of workgroups, each taking every (nwg/8)-th id of its XCD's
+run) computes every tile exactly once, and so do the per-XCD queues with stealing
+(queue_next), under random interleavings of the workgroups' takes and with
+workgroups that keep taking after every run is empty."""
 import os
 import shutil
 import subprocess
@@ -67,6 +69,34 @@ int main(int argc, char** argv) {
       }
     }
     for (int i = 0; i < total; ++i) if (hit[i] != 1) { printf("chain tile %d hit %d\n", i, hit[i]); return 1; }
+  }
+  // the queues: workgroups on random XCDs take ids in a random order (every XCD's
+  // own run first, then the others'), each until it gets -1; every id is handed
+  // out once, and an XCD steals only once its own run is empty
+  for (int trial = 0; trial < 4; ++trial) {
+    unsigned rng = 12345u + 977u * (unsigned)trial + (unsigned)total;
+    auto rnd = [&rng]() { rng = rng * 1664525u + 1013904223u; return rng >> 8; };
+    int counter[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    std::vector<int> hit(total, 0);
+    const int wgs = 8 * (1 + (int)(rnd() % 40));
+    std::vector<int> done(wgs, 0);
+    int live = wgs;
+    while (live > 0) {
+      const int b = (int)(rnd() % wgs);
+      if (done[b]) continue;
+      const int xcd = b & 7;
+      int own_start, own_len;
+      gh::xcd_run(xcd, total, own_start, own_len);
+      const bool own_left = counter[xcd] < own_len;
+      auto take = [&counter](int x) { return counter[x]++; };
+      const int id = gh::queue_next(take, xcd, total);
+      if (id < 0) { done[b] = 1; --live; continue; }
+      if (id >= total) { printf("queue id out of range\n"); return 1; }
+      const bool own = id >= own_start && id < own_start + own_len;
+      if (own_left != own) { printf("stole while the own run had ids\n"); return 1; }
+      hit[id]++;
+    }
+    for (int i = 0; i < total; ++i) if (hit[i] != 1) { printf("queue id %d hit %d\n", i, hit[i]); return 1; }
   }
   printf("ok\n");
   return 0;
