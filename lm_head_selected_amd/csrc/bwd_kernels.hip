@@ -32,8 +32,9 @@
 // dz is stored "v-blocked": [vocabulary / 64][chunk rows][64], so a K stage of the
 // dH product (256 rows x 64 vocabulary entries, bf16) is one contiguous 32 KB run,
 // and a K stage of the dW product (64 rows x 256 entries) four runs of 8 KB.  (A
-// layout blocked by 256, whose dH stages are 256 runs of 128 B, 512 B apart,
-// measured 0.18 ms slower in the gradient launch.)
+// layout blocked by 256, whose dH stages are 256 runs of 128 B, 512 B apart and
+// whose dW stages are one 32 KB run, measured 0.07 ms slower in the gradient launch
+// and 0.02 ms faster in dlogits.)
 #include <type_traits>
 
 #include "gemm_tile.hpp"
