@@ -74,6 +74,8 @@ struct DlogitsArgs {
   int group_m;
   const int32_t* live;            // live row count (device); token tiles past it are skipped
   const int32_t* ytg;             // [dz_rows] target id of each row, -1 where there is none
+  int32_t* queue;                 // [8] tile queues of the chained launch (cleared by the
+                                  // compaction)
 };
 
 // Row compaction of one chunk (blocks of kCompactBlock tokens, one per thread).
@@ -91,7 +93,8 @@ struct CompactArgs {
                       // the counts before it itself (few blocks)
   int64_t v_real;
   int32_t* ytg;       // [n_pad] target id of compact row r if in [0, v_real), else -1
-  int32_t* dwq;       // [8] the gradient launch's dW tile queues, cleared here
+  int32_t* dwq;       // [16] the tile queues of the dlogits launch ([0, 8)) and of the
+                      // gradient launch's dW tiles ([8, 16)), cleared here
 };
 
 // g_t = grad_output * coef_t / tau for an active token, 0 otherwise.  A token is
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(kCompactBlock) void compact_kernel(CompactArgs a) {
     int total = base;
     for (int w = 0; w < kCompactWaves; ++w) total += wcnt[w];
     if (threadIdx.x == 0) *a.live = total;
-    if (threadIdx.x < 8) a.dwq[threadIdx.x] = 0;
+    if (threadIdx.x < 16) a.dwq[threadIdx.x] = 0;
     for (int64_t r = total + threadIdx.x; r < a.n_pad; r += kCompactBlock) {
       a.rows[r] = -1;
       a.gl[r] = make_float2(0.0f, 0.0f);
@@ -301,6 +304,168 @@ __global__ __launch_bounds__(kThreads) void dlogits_kernel(DlogitsArgs a, int ti
   }
 }
 
+// The chained dlogits launch: one workgroup per compute unit, each taking logit
+// tiles (of the token tiles holding live rows) from per-XCD queues, with the K
+// pipeline running on from one tile into the next (gemm_tile_chain), as the
+// forward's tile launch does.  The epilogue runs while the next tile's first loads
+// land in the pipeline buffers, so it keeps to the LDS past them:
+//  - a tile's per-token values, (g, lse log2 e) then the target id (3 KB), arrive by
+//    direct-to-LDS loads that wave 0 issues at the start of the tile before, in three
+//    buffers in turn (a wave may still read the previous tile's while wave 0 loads
+//    the next one's);
+//  - bf16: each wave passes its 128 (vocabulary) x 64 (token) sub-tile through its own
+//    2 KB slice, 8 passes of 16 token rows x 64 entries (one v-block), with no
+//    workgroup barrier, and writes each row's 64 entries as one 128-byte run; fp32
+//    stores straight from the accumulators.
+// Each tile's values are those of dlogits_kernel, bit for bit.
+constexpr int kDlSlice = 2048;
+constexpr int kDlTok = kTile * 12;
+constexpr int kDlChainLds = kGemmLds + kWaves * kDlSlice + 3 * kDlTok + 8 * (int)sizeof(int32_t);
+
+template <typename T>
+__device__ __forceinline__ void dlogits_epilogue_wave(f32x4 (&acc)[kBI][kBJ],
+                                                      const DlogitsArgs& a, int64_t v0,
+                                                      int64_t t0, const char* tok,
+                                                      lds_t* slice) {
+  // (the lane index made opaque, so that nothing derived from it is hoisted out of
+  // the tile loop, where it would stay live across the K loop)
+  int lane = threadIdx.x & 63;
+  __asm__ volatile("" : "+v"(lane));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / kWN, wn = wave % kWN;
+  if (v0 + kTile > a.v_real) {   // uniform per workgroup: only the ragged vocabulary tile
+    const int64_t left = a.v_real - (v0 + wm * (kTile / kWM));
+    mask_rows(acc, (int)(left < 0 ? 0 : (left > 128 ? 128 : left)));
+  }
+  const int64_t esz = Elem<T>::size;
+  const int64_t block_bytes = a.dz_rows * 64 * esz;   // between 64-element blocks
+  const float c2 = a.inv_tau * kLog2e;
+  const int qg = lane >> 4;
+  const int vl = wm * (kTile / kWM) + qg * 4;         // tile-local vocabulary row
+  // this tile's part of dz: rows t0 .. t0 + 255 of the 4 vocabulary blocks from v0 / 64
+  char* dzt = (char*)a.dz + vblocked_offset(t0, v0, a.dz_rows, esz);
+  const int wr = lane & 15;                           // token row written by this lane
+  auto column = [&](int j, int tl, float g, float lse2, int32_t rel, bool own, auto fix) {
+    constexpr bool kFix = decltype(fix)::value;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int ii = 0; ii < kBI / 2; ++ii) {
+        const int i = h * (kBI / 2) + ii;
+        float d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = fast_exp2(acc[i][j][e] * c2 - lse2);
+          d[e] = -g * p;
+          if (kFix) d[e] = (own && rel == i * 16 + qg * 4 + e) ? g * (1.0f - p) : d[e];
+        }
+        if (sizeof(T) == 2) {
+          // token row wr, entries ii * 16 + qg * 4 .. + 3 of the pass's 64
+          const bf16x4 q = {(__bf16)d[0], (__bf16)d[1], (__bf16)d[2], (__bf16)d[3]};
+          const int c = ii * 2 + (qg >> 1);
+          *(__attribute__((address_space(3))) i32x2*)(
+              slice + wr * 128 + ((c ^ ((wr >> 1) & 7)) << 4) + (qg & 1) * 8) =
+              __builtin_bit_cast(i32x2, q);
+        } else {
+          const int v = vl + i * 16;                  // 4 consecutive v
+          Store4<T>::run(dzt + (v >> 6) * block_bytes + (int64_t)tl * 64 * esz + (v & 63) * esz,
+                         d[0], d[1], d[2], d[3]);
+        }
+      }
+      if (sizeof(T) == 2) {
+        lgkm_drain();
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int rr = u * 8 + (lane >> 3), c = lane & 7;
+          const i32x4 v = *(const __attribute__((address_space(3))) i32x4*)(
+              slice + rr * 128 + ((c ^ ((rr >> 1) & 7)) << 4));
+          const int64_t t = wn * (kTile / kWN) + j * 16 + rr;   // tile-local token row
+          __builtin_nontemporal_store(
+              v, (i32x4*)(dzt + (wm * 2 + h) * block_bytes + t * 128 + c * 16));
+        }
+        lgkm_drain();
+      }
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kBJ; ++j) {
+    const int tl = wn * (kTile / kWN) + j * 16 + wr;      // tile-local token
+    const f32x2 glv = *(const __attribute__((address_space(3))) f32x2*)(tok + tl * 8);
+    const int32_t yt = *(const __attribute__((address_space(3))) int32_t*)(tok + 2048 + tl * 4);
+    const float g = glv[0];
+    const float lse2 = glv[1];
+    const int32_t rel = yt - (int32_t)(v0 + wm * (kTile / kWM));
+    const bool own = yt >= 0 && (uint32_t)rel < (uint32_t)(kTile / kWM) && ((rel >> 2) & 3) == qg;
+    if (__builtin_amdgcn_ballot_w64(own) != 0)
+      column(j, tl, g, lse2, rel, own, std::true_type{});
+    else
+      column(j, tl, g, lse2, rel, own, std::false_type{});
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void dlogits_chain_kernel(DlogitsArgs a, int tiles_m,
+                                                                 int tiles_n) {
+  __shared__ __attribute__((aligned(16))) char lds[kDlChainLds];
+  const int live_n = (int)ceil_div((int64_t)*a.live, kTile);
+  if (live_n < tiles_n) tiles_n = live_n;
+  if (tiles_n <= 0) return;
+  const int xcd = (int)blockIdx.x & 7;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  char* tokbuf = lds + kGemmLds + kWaves * kDlSlice;
+  int32_t* ring_m = (int32_t*)(tokbuf + 3 * kDlTok);
+  int32_t* ring_n = ring_m + 4;
+  lds_t* slice = (lds_t*)(lds + kGemmLds + wave * kDlSlice);
+  const int64_t esz = Elem<T>::size;
+  const int nk = (int)(a.d_model * esz / kStageBytes);
+  const Operand A = nt_row_major(a.W, a.d_model * esz, a.v_real);
+  const Operand B = nt_row_major(a.H, a.d_model * esz, a.chunk_tokens);
+  // wave 0 loads token tile tn's (g, lse2) (2 KB; rows past the chunk read zeros) and
+  // target ids (1 KB) into buffer q
+  auto load_tok = [&](int tn, int q) {
+    if (wave != 0) return;
+    uint32_t ln = threadIdx.x & 63;
+    __asm__ volatile("" : "+v"(ln));
+    const __amdgpu_buffer_rsrc_t rg = range_rsrc((const char*)a.gl, a.chunk_tokens * 8);
+    const __amdgpu_buffer_rsrc_t ry = range_rsrc((const char*)a.ytg, a.dz_rows * 4);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tokbuf + q * kDlTok));
+    const uint32_t r0 = (uint32_t)tn * kTile;
+    dma16(rg, r0 * 8 + ln * 16, 0u, dst);
+    dma16(rg, r0 * 8 + 1024 + ln * 16, 0u, dst + 1024);
+    dma16(ry, r0 * 4 + ln * 16, 0u, dst + 2048);
+  };
+  if (threadIdx.x == 0)
+    for (int q = 0; q < 3; ++q)
+      grab_tile(a.queue, xcd, tiles_m, tiles_n, a.group_m, ring_m[q], ring_n[q]);
+  __syncthreads();
+  int tm = ring_m[0], tn = ring_n[0];
+  int tmn = ring_m[1], tnn = ring_n[1];
+  if (tm < 0) return;
+  load_tok(tn, 0);
+  i32x4 fa0[kBI], fb0[kBJ];
+  for (int k = 0;; ++k) {
+    const bool has_next = tmn >= 0;
+    if (has_next) load_tok(tnn, (k + 1) % 3);
+    const int64_t v0 = (int64_t)tm * kTile, t0 = (int64_t)tn * kTile;
+    f32x4 acc[kBI][kBJ];
+    zero_acc(acc);
+    gemm_tile_chain<T>(A, B, v0, t0, has_next, (int64_t)tmn * kTile, (int64_t)tnn * kTile, nk,
+                       k == 0, (lds_t*)lds, acc, fa0, fb0);
+    int am = -1, an = 0;
+    if (threadIdx.x == 0) grab_tile(a.queue, xcd, tiles_m, tiles_n, a.group_m, am, an);
+    dlogits_epilogue_wave<T>(acc, a, v0, t0, tokbuf + (k % 3) * kDlTok, slice);
+    if (threadIdx.x == 0) {
+      ring_m[(k + 3) & 3] = am;
+      ring_n[(k + 3) & 3] = an;
+    }
+    if (!has_next) break;
+    tm = tmn;
+    tn = tnn;
+    tmn = ring_m[(k + 2) & 3];
+    tnn = ring_n[(k + 2) & 3];
+  }
+}
+
 // Products with a K-contiguous A and an MN-contiguous B.
 //   dH: C[m = live row r][n = d] stored row-major at the row's token:
 //       out[out_rows[m] * ld_out + n];
@@ -393,8 +558,8 @@ __device__ __forceinline__ void store_dw_tile_wave(const f32x4 (&acc)[kBI][kBJ],
   // (the lane index made opaque, so that nothing derived from it is hoisted out of
   // the caller's tile loop, where it would stay live across the K loop)
   int lane = threadIdx.x & 63;
-  __asm__("" : "+v"(lane));
-  const int wave = threadIdx.x >> 6;
+  __asm__ volatile("" : "+v"(lane));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / kWN, wn = wave % kWN;
   int64_t rows = n_limit - n0;
   rows = rows < 0 ? 0 : (rows > kTile ? kTile : rows);
@@ -698,10 +863,20 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(zero_dead_rows_kernel<O>, dim3((unsigned)ceil_div(nc, 4)), dim3(256), 0, s,
                        (const int32_t*)rowpos, nc, D, dH + c0 * D);
 
-    DlogitsArgs d{a.W, hg, gl, nc, D, a.v_real, a.inv_tau, dz, R, a.group_dlogits, live, ytg};
+    DlogitsArgs d{a.W, hg, gl, nc, D, a.v_real, a.inv_tau, dz, R, a.group_dlogits, live, ytg,
+                  dwq};
+    const int dl_nk = (int)(D * esz / kStageBytes);
+    const int cus = chain_workgroups();
     ev.mark(5, s);
-    hipLaunchKernelGGL(dlogits_kernel<T>, dim3(tiles_v * tiles_t), dim3(kThreads), 0, s, d,
-                       tiles_v, tiles_t);
+    if (dl_nk % 2 == 0 && cus >= 8) {
+      const int tiles = tiles_v * tiles_t;
+      const int dl_wgs = tiles < cus ? (int)ceil_div(tiles, 8) * 8 : cus;
+      hipLaunchKernelGGL(dlogits_chain_kernel<T>, dim3(dl_wgs), dim3(kThreads), 0, s, d, tiles_v,
+                         tiles_t);
+    } else {
+      hipLaunchKernelGGL(dlogits_kernel<T>, dim3(tiles_v * tiles_t), dim3(kThreads), 0, s, d,
+                         tiles_v, tiles_t);
+    }
     ev.mark(6, s);
 
     // dH rows of the chunk: M = live row r (dz rows), N = d (W read MN-contiguous),
@@ -724,7 +899,7 @@ static hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
     if (dw_wgs < 8) dw_wgs = 8;
     if (dw_wgs > dw_tiles) dw_wgs = (int)ceil_div(dw_tiles, 8) * 8;
     hipLaunchKernelGGL((grad_products_kernel<T, O>), dim3(dh_slots + dw_wgs), dim3(kThreads), 0,
-                       s, ph, pw, dwq, dh_slots, tiles_t, tiles_d, tiles_d, tiles_v);
+                       s, ph, pw, dwq + 8, dh_slots, tiles_t, tiles_d, tiles_d, tiles_v);
     ev.mark(7, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

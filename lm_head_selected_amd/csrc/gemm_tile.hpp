@@ -631,7 +631,7 @@ __device__ __forceinline__ void gemm_tile_chain_split(const Operand& A, const Op
   // (the lane index made opaque: the per-lane offsets below are then formed on each
   // call rather than hoisted out of the caller's tile loop and kept across it)
   int lane = tid & 63;
-  __asm__("" : "+v"(lane));
+  __asm__ volatile("" : "+v"(lane));
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kWN, wn = wave % kWN;
 

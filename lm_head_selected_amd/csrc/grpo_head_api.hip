@@ -146,7 +146,7 @@ gh::WsLayout layout(const grpo_head_params* p, bool with_gemm = true) {
   L.rowpos = take((size_t)chunk * 4);
   L.hg = take((size_t)chunk * D * esz);       // the chunk's live H rows
   L.ytg = take((size_t)chunk * 4);            // target id of each compact row
-  L.dwq = take(8 * 4);                        // dW tile queues of the gradient launch
+  L.dwq = take(16 * 4);                       // tile queues of dlogits and of the dW tiles
   L.bwd_bytes = off > L.fwd_bytes ? off : L.fwd_bytes;
   return L;
 }

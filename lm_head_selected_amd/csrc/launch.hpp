@@ -27,7 +27,8 @@ struct WsLayout {
   // token indices, every token's compact row (-1 if dead), the gathered H rows and
   // each compact row's target id
   size_t bcnt = 0, live = 0, rows = 0, rowpos = 0, hg = 0, ytg = 0;
-  // the dW tile queues of the gradient launch: one counter per XCD
+  // the tile queues of the dlogits launch and of the gradient launch's dW tiles:
+  // one counter per XCD each
   size_t dwq = 0;
   size_t bwd_bytes = 0;
   int64_t n_vt = 0;        // vocabulary tiles covering [0, v_real)
