@@ -452,9 +452,9 @@ __global__ __launch_bounds__(kThreads) void dlogits_chain_kernel(DlogitsArgs a, 
     gemm_tile_chain<T>(A, B, v0, t0, has_next, (int64_t)tmn * kTile, (int64_t)tnn * kTile, nk,
                        k == 0, (lds_t*)lds, acc, fa0, fb0);
     int am = -1, an = 0;
-    if (threadIdx.x == 0) grab_tile(a.queue, xcd, tiles_m, tiles_n, a.group_m, am, an);
+    if (threadIdx.x == kGrabThread) grab_tile(a.queue, xcd, tiles_m, tiles_n, a.group_m, am, an);
     dlogits_epilogue_wave<T>(acc, a, v0, t0, tokbuf + (k % 3) * kDlTok, slice);
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == kGrabThread) {
       ring_m[(k + 3) & 3] = am;
       ring_n[(k + 3) & 3] = an;
     }

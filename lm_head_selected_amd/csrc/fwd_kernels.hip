@@ -122,9 +122,10 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_kernel(FwdTileArgs a, int t
 // resident together on an XCD are the same as with one workgroup per tile.
 // kQueue: the workgroups take the ids from per-XCD queues (grab_tile), and an XCD
 // that empties its run takes ids from the others' runs, which balances XCDs that
-// run at different clocks (a few percent apart); thread 0 takes each id three
+// run at different clocks (a few percent apart); one thread takes each id three
 // tiles ahead and passes it on through a ring of four LDS slots, as the dW tiles
-// of the backward do.  Without kQueue (no queue memory: the vocabulary-shard
+// of the backward do (here the thread is in wave 4, which issues no loads, so
+// waiting for the queue access does not wait for the next tile's loads).  Without kQueue (no queue memory: the vocabulary-shard
 // entry) workgroup b takes every (per-XCD count)-th id of its run from b / 8 on.
 // Needs an even number of K stages.
 template <typename T, bool kQueue>
@@ -159,9 +160,9 @@ __global__ __launch_bounds__(kThreads) void fwd_tile_chain_kernel(FwdTileArgs a,
       gemm_tile_chain<T>(A, B, v0, t0, has_next, (int64_t)tmn * kTile, (int64_t)tnn * kTile,
                          nk, k == 0, (lds_t*)lds, acc, fa0, fb0);
       int am = -1, an = 0;
-      if (threadIdx.x == 0) grab_tile(queue, xcd, tiles_m, tiles_n, a.group_m, am, an);
+      if (threadIdx.x == kGrabThread) grab_tile(queue, xcd, tiles_m, tiles_n, a.group_m, am, an);
       tile_partials<true>(acc, a, tm, v0, t0, half_stats);
-      if (threadIdx.x == 0) {
+      if (threadIdx.x == kGrabThread) {
         ring_m[(k + 3) & 3] = am;
         ring_n[(k + 3) & 3] = an;
       }

@@ -726,6 +726,12 @@ __device__ __forceinline__ void gemm_tile_chain_split(const Operand& A, const Op
   }
 }
 
+// The thread that takes the next tile of a persistent launch whose loads only
+// waves 0-3 issue (the logit products): lane 0 of wave 4.  Its wave has no load in
+// flight, so waiting for the queue access never waits for the next tile's loads
+// (memory operations complete in issue order per wave).
+constexpr int kGrabThread = 4 * 64;
+
 // The next tile of a persistent launch for a workgroup on XCD `xcd` (queue_next:
 // its own XCD's run of logical ids first, then the other XCDs'), as (M tile,
 // N tile), or tm = -1 once every run is handed out.  queue[x] counts the ids handed
