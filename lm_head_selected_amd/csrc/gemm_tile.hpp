@@ -157,11 +157,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(const Operand& op,
 }
 
 // Byte stride between consecutive K stages of an operand whose stages are evenly
-// spaced: an MN-contiguous operand, or a K-contiguous one stored row-major (no
-// grouping of stages).  The chained tile core takes only such operands.
+// spaced: an MN-contiguous operand, a K-contiguous one stored row-major (no
+// grouping of stages), or a K-contiguous one with one stage per group (the
+// v-blocked dz in bf16).  The split-issue tile core takes only such operands.
 template <typename T>
 __device__ __forceinline__ int64_t stage_stride(const Operand& op, bool mn) {
-  return mn ? (int64_t)(kStageBytes / (int)sizeof(T)) * op.ld : (int64_t)kStageBytes;
+  if (mn) return (int64_t)(kStageBytes / (int)sizeof(T)) * op.ld;
+  return op.group_shift == 0 ? op.group_bytes : (int64_t)kStageBytes;
 }
 
 // Buffer resource over `limit` bytes from `base` (none if limit <= 0; at most
@@ -610,9 +612,11 @@ __device__ __forceinline__ void gemm_tile_chain(const Operand& A, const Operand&
   }
 }
 
-// gemm_tile_chain for a K-contiguous A stored row-major and an MN-contiguous B
-// blocked by 64 elements (the dW product), with the loads split as gemm_tile splits them for these operands:
-// waves 0-3 load B, waves 4-7 A.  Each wave's operand is a plain stream of stages
+// gemm_tile_chain for a K-contiguous A whose stages are evenly spaced and an
+// MN-contiguous B, blocked by 64 elements (kBlockedB: the dW product) or row-major
+// (the dH product, which calls it for single tiles: has_next false, first true),
+// with the loads split as gemm_tile splits them for these operands: waves 0-3
+// load B, waves 4-7 A.  Each wave's operand is a plain stream of stages
 // at a fixed byte stride, selected once, and its eight loads of a stage go out
 // as one asm block, which keeps the scalar registers the loop needs within the
 // file (with the generic stage addressing of gemm_tile the compiler spilled
@@ -620,7 +624,7 @@ __device__ __forceinline__ void gemm_tile_chain(const Operand& A, const Operand&
 // caller's epilogue stores, which were issued after the next tile's stage-1 loads:
 // letting them stay in flight there, with a second wait count for the first stage,
 // likewise made the compiler spill.
-template <typename T>
+template <typename T, bool kBlockedB = true>
 __device__ __forceinline__ void gemm_tile_chain_split(const Operand& A, const Operand& B,
                                                       int64_t m0, int64_t n0, bool has_next,
                                                       int64_t m0n, int64_t n0n, int nk,
@@ -649,8 +653,8 @@ __device__ __forceinline__ void gemm_tile_chain_split(const Operand& A, const Op
   uint32_t stepA, stepB;
   const uint32_t offA0 = load_offset<T>(A, lw, lane, stepA);
   const uint32_t offA1 = load_offset<T>(A, lw + kHalf, lane, stepA);
-  const uint32_t offB0 = load_offset<T, 1>(B, lw, lane, stepB);
-  const uint32_t offB1 = load_offset<T, 1>(B, lw + kHalf, lane, stepB);
+  const uint32_t offB0 = load_offset<T, kBlockedB ? 1 : 0>(B, lw, lane, stepB);
+  const uint32_t offB1 = load_offset<T, kBlockedB ? 1 : 0>(B, lw + kHalf, lane, stepB);
   // the one operand this wave loads, as a stream of stages at a fixed byte stride
   const int64_t sstride = firstw ? stage_stride<T>(B, true) : stage_stride<T>(A, false);
   const char* sbase = firstw ? tb.base : ta.base;
@@ -667,7 +671,8 @@ __device__ __forceinline__ void gemm_tile_chain_split(const Operand& A, const Op
     const int64_t o = (int64_t)ks * sstride;
     const __amdgpu_buffer_rsrc_t r =
         range_rsrc((nxt ? sbase_n : sbase) + o, (nxt ? slimit_n : slimit) - o);
-    dma16_split(r, so0, so1, sstep, __builtin_amdgcn_readfirstlane(s0 + sregion));
+    dma16_split(r, so0, so1, __builtin_amdgcn_readfirstlane(sstep),
+                __builtin_amdgcn_readfirstlane(s0 + sregion));
   };
   auto quarter = [&](const i32x4 (&ca)[kBI], const i32x4 (&cb)[kBJ], i32x4 (&na)[kBI],
                      i32x4 (&nb)[kBJ], int rstage, int rks, int c) {
