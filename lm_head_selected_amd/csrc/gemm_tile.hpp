@@ -503,7 +503,8 @@ __device__ __forceinline__ void gemm_tile(const Operand& A, const Operand& B, in
   pipe_barrier();
 }
 
-// gemm_tile for two K-contiguous operands, chained across the tiles one workgroup
+// gemm_tile for two K-contiguous row-major operands (nt_row_major: stage s sits
+// s x kStageBytes into each tile's range), chained across the tiles one workgroup
 // computes in turn (an even number of K stages, so stage s of every tile sits in
 // LDS buffer s % 2).  The loads that gemm_tile spends on the two stages past the
 // end of K fetch the next tile's stages 0 and 1 instead, and the last fragment
@@ -541,22 +542,17 @@ __device__ __forceinline__ void gemm_tile_chain(const Operand& A, const Operand&
   auto issue = [&](int stage) {
     if (wave >= kHalf) return;
     const uint32_t s0 = lds_base + (stage & 1) * kStageLds + lw * 1024;
-    const uint32_t s1 = s0 + kHalf * 1024;
     const bool nxt = has_next && stage >= nk;
     const int ks = nxt ? stage - nk : stage;
-    const __amdgpu_buffer_rsrc_t ra = stage_rsrc<T>(A, nxt ? tan : ta, ks);
-    const __amdgpu_buffer_rsrc_t rb = stage_rsrc<T>(B, nxt ? tbn : tb, ks);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const uint32_t ia = __builtin_amdgcn_readfirstlane(i * stepA);
-      const uint32_t ib = __builtin_amdgcn_readfirstlane(i * stepB);
-      const uint32_t l0 = __builtin_amdgcn_readfirstlane(s0 + i * kWaves * 1024);
-      const uint32_t l1 = __builtin_amdgcn_readfirstlane(s1 + i * kWaves * 1024);
-      dma16(ra, offA0, ia, l0);
-      dma16(rb, offB0, ib, l0 + kOpLds);
-      dma16(ra, offA1, ia, l1);
-      dma16(rb, offB1, ib, l1 + kOpLds);
-    }
+    // both operands K-contiguous: a stage starts kStageBytes further along each tile's
+    // range, and each operand's eight loads go out in one asm block
+    const int64_t o = (int64_t)ks * kStageBytes;
+    const TileRange xa = nxt ? tan : ta, xb = nxt ? tbn : tb;
+    const __amdgpu_buffer_rsrc_t ra = range_rsrc(xa.base + o, xa.limit - o);
+    const __amdgpu_buffer_rsrc_t rb = range_rsrc(xb.base + o, xb.limit - o);
+    const uint32_t l = __builtin_amdgcn_readfirstlane(s0);
+    dma16_split(ra, offA0, offA1, __builtin_amdgcn_readfirstlane(stepA), l);
+    dma16_split(rb, offB0, offB1, __builtin_amdgcn_readfirstlane(stepB), l + kOpLds);
   };
   auto quarter = [&](const i32x4 (&ca)[kBI], const i32x4 (&cb)[kBJ], i32x4 (&na)[kBI],
                      i32x4 (&nb)[kBJ], int rstage, int rks, int c) {
