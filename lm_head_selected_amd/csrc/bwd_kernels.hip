@@ -613,13 +613,13 @@ __device__ __forceinline__ void dh_tile(const ProductArgs& a, int bid, int tiles
   f32x4 acc[kBI][kBJ];
   zero_acc(acc);
   if constexpr (sizeof(T) == 2) {
-    // the split-issue core of the dW tiles (its stage streams and one asm block per
-    // stage's loads) also runs dH faster than gemm_tile: 14.46 -> 14.36 ms for the
-    // gradient launch (three alternating pairs).  The fp32 dz blocks hold two stages
-    // each, which that core's fixed stage stride does not cover.
+    // the chained core of the dW tiles (its stage streams and one asm block per
+    // operand's stage loads) also runs dH faster than gemm_tile: 14.46 -> 14.36 ms
+    // for the gradient launch (three alternating pairs).  The fp32 dz blocks hold two
+    // stages each, which that core's fixed stage stride does not cover.
     i32x4 fa0[kBI], fb0[kBJ];
-    gemm_tile_chain_split<T, false>(a.A, a.B, m0, n0, false, m0, n0, a.nk, true, (lds_t*)lds,
-                                    acc, fa0, fb0);
+    gemm_tile_chain_mn<T, false>(a.A, a.B, m0, n0, false, m0, n0, a.nk, true, (lds_t*)lds,
+                                 acc, fa0, fb0);
   } else {
     gemm_tile<T, false, true>(a.A, a.B, m0, n0, a.nk, (lds_t*)lds, acc);
   }
@@ -651,7 +651,7 @@ __device__ __forceinline__ void dh_tile(const ProductArgs& a, int bid, int tiles
 // The dW tiles, C[m = d][n = v] = sum over the live rows r of HT[d][r] dz[r][v],
 // stored as out[n * ld_out + m]: each of a fixed number of workgroups takes tiles
 // from the queues until none is left, with the K pipeline running on from one
-// tile into the next (gemm_tile_chain_split), so a tile's epilogue overlaps the next
+// tile into the next (gemm_tile_chain_mn), so a tile's epilogue overlaps the next
 // tile's first loads.
 // The K loop runs over the stages covering the live rows, rounded up to an even
 // count (the rows past the live count up to the next 256 are zero in both
@@ -703,8 +703,8 @@ __device__ __forceinline__ void dw_tiles(const ProductArgs& a, int32_t* queue, i
     const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
     f32x4 acc[kBI][kBJ];
     zero_acc(acc);
-    gemm_tile_chain_split<T>(a.A, a.B, m0, n0, has_next, (int64_t)tmn * kTile,
-                             (int64_t)tnn * kTile, nk, k == 0, (lds_t*)lds, acc, fa0, fb0);
+    gemm_tile_chain_mn<T>(a.A, a.B, m0, n0, has_next, (int64_t)tmn * kTile,
+                          (int64_t)tnn * kTile, nk, k == 0, (lds_t*)lds, acc, fa0, fb0);
     // (taken before the epilogue's stores, so waiting for it waits for nothing that
     // the next tile's first K stage does not wait for anyway)
     int am = -1, an = 0;

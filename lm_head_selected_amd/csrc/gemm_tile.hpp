@@ -159,7 +159,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(const Operand& op,
 // Byte stride between consecutive K stages of an operand whose stages are evenly
 // spaced: an MN-contiguous operand, a K-contiguous one stored row-major (no
 // grouping of stages), or a K-contiguous one with one stage per group (the
-// v-blocked dz in bf16).  The split-issue tile core takes only such operands.
+// v-blocked dz in bf16).  gemm_tile_chain_mn takes only such operands.
 template <typename T>
 __device__ __forceinline__ int64_t stage_stride(const Operand& op, bool mn) {
   if (mn) return (int64_t)(kStageBytes / (int)sizeof(T)) * op.ld;
@@ -194,7 +194,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voffset
                    : "v"(voffset), "s"(r), "s"(soffset), "s"(lds_addr)
                    : "memory", "m0");
 }
-// One wave's share of a stage of one operand under the split issue: kLoads pairs of
+// One wave's share of a stage of one operand in the chained cores: kLoads pairs of
 // loads (lane offsets o0 and o1, the pair's K rows i * step further on), filling
 // the 1 KB LDS blocks lds_addr, + 4 KB, + 8 KB, ... in turn.  One asm block that
 // steps M0 and the scalar offset itself, so the eight destinations take no
@@ -610,23 +610,23 @@ __device__ __forceinline__ void gemm_tile_chain(const Operand& A, const Operand&
 
 // gemm_tile_chain for a K-contiguous A whose stages are evenly spaced and an
 // MN-contiguous B, blocked by 64 elements (kBlockedB: the dW product) or row-major
-// (the dH product, which calls it for single tiles: has_next false, first true),
-// with the loads split as gemm_tile splits them for these operands: waves 0-3
-// load B, waves 4-7 A.  Each wave's operand is a plain stream of stages
-// at a fixed byte stride, selected once, and its eight loads of a stage go out
-// as one asm block, which keeps the scalar registers the loop needs within the
-// file (with the generic stage addressing of gemm_tile the compiler spilled
-// registers in the loop).  The first wait of a chained call also waits for the
-// caller's epilogue stores, which were issued after the next tile's stage-1 loads:
-// letting them stay in flight there, with a second wait count for the first stage,
-// likewise made the compiler spill.
+// (the dH product, which calls it for single tiles: has_next false, first true).
+// Each operand is a plain stream of stages at a fixed byte stride, and waves 0-3
+// issue every load, each operand's eight loads of a stage as one asm block, as in
+// gemm_tile_chain.  With gemm_tile's generic stage addressing the compiler
+// spilled registers in this loop; with one asm block per stage the waves 0-3
+// issue pays off for these operands too (the gradient launch 13.90 -> 13.72 ms
+// against waves 0-3 loading B and waves 4-7 A, in alternating runs).  The first
+// wait of a chained call also waits for the caller's epilogue stores, which were
+// issued after the next tile's stage-1 loads: letting them stay in flight there,
+// with a second wait count for the first stage, made the compiler spill.
 template <typename T, bool kBlockedB = true>
-__device__ __forceinline__ void gemm_tile_chain_split(const Operand& A, const Operand& B,
-                                                      int64_t m0, int64_t n0, bool has_next,
-                                                      int64_t m0n, int64_t n0n, int nk,
-                                                      bool first, lds_t* lds,
-                                                      f32x4 (&acc)[kBI][kBJ],
-                                                      i32x4 (&fa0)[kBI], i32x4 (&fb0)[kBJ]) {
+__device__ __forceinline__ void gemm_tile_chain_mn(const Operand& A, const Operand& B,
+                                                   int64_t m0, int64_t n0, bool has_next,
+                                                   int64_t m0n, int64_t n0n, int nk,
+                                                   bool first, lds_t* lds,
+                                                   f32x4 (&acc)[kBI][kBJ],
+                                                   i32x4 (&fa0)[kBI], i32x4 (&fb0)[kBJ]) {
   const int tid = threadIdx.x;
   // (the lane index made opaque: the per-lane offsets below are then formed on each
   // call rather than hoisted out of the caller's tile loop and kept across it)
@@ -642,33 +642,27 @@ __device__ __forceinline__ void gemm_tile_chain_split(const Operand& A, const Op
   const uint32_t lds_base = (uint32_t)(uintptr_t)lds;
 
   // stages nk and nk + 1 come from the next tile when there is one; waves 0-3 load
-  // B, waves 4-7 A, each the shares of waves lw and lw + 4
+  // both operands, each the shares of waves lw and lw + 4
   constexpr int kHalf = kWaves / 2;
   const int lw = wave & (kHalf - 1);
-  const bool firstw = wave < kHalf;
   uint32_t stepA, stepB;
   const uint32_t offA0 = load_offset<T>(A, lw, lane, stepA);
   const uint32_t offA1 = load_offset<T>(A, lw + kHalf, lane, stepA);
   const uint32_t offB0 = load_offset<T, kBlockedB ? 1 : 0>(B, lw, lane, stepB);
   const uint32_t offB1 = load_offset<T, kBlockedB ? 1 : 0>(B, lw + kHalf, lane, stepB);
-  // the one operand this wave loads, as a stream of stages at a fixed byte stride
-  const int64_t sstride = firstw ? stage_stride<T>(B, true) : stage_stride<T>(A, false);
-  const char* sbase = firstw ? tb.base : ta.base;
-  const char* sbase_n = firstw ? tbn.base : tan.base;
-  const int64_t slimit = firstw ? tb.limit : ta.limit;
-  const int64_t slimit_n = firstw ? tbn.limit : tan.limit;
-  const uint32_t so0 = firstw ? offB0 : offA0, so1 = firstw ? offB1 : offA1;
-  const uint32_t sstep = firstw ? stepB : stepA;
-  const uint32_t sregion = firstw ? (uint32_t)kOpLds : 0u;
+  const int64_t strideA = stage_stride<T>(A, false), strideB = stage_stride<T>(B, true);
   auto issue = [&](int stage) {
+    if (wave >= kHalf) return;
     const uint32_t s0 = lds_base + (stage & 1) * kStageLds + lw * 1024;
     const bool nxt = has_next && stage >= nk;
     const int ks = nxt ? stage - nk : stage;
-    const int64_t o = (int64_t)ks * sstride;
-    const __amdgpu_buffer_rsrc_t r =
-        range_rsrc((nxt ? sbase_n : sbase) + o, (nxt ? slimit_n : slimit) - o);
-    dma16_split(r, so0, so1, __builtin_amdgcn_readfirstlane(sstep),
-                __builtin_amdgcn_readfirstlane(s0 + sregion));
+    const TileRange xa = nxt ? tan : ta, xb = nxt ? tbn : tb;
+    const int64_t oa = (int64_t)ks * strideA, ob = (int64_t)ks * strideB;
+    const __amdgpu_buffer_rsrc_t ra = range_rsrc(xa.base + oa, xa.limit - oa);
+    const __amdgpu_buffer_rsrc_t rb = range_rsrc(xb.base + ob, xb.limit - ob);
+    const uint32_t l = __builtin_amdgcn_readfirstlane(s0);
+    dma16_split(ra, offA0, offA1, __builtin_amdgcn_readfirstlane(stepA), l);
+    dma16_split(rb, offB0, offB1, __builtin_amdgcn_readfirstlane(stepB), l + kOpLds);
   };
   auto quarter = [&](const i32x4 (&ca)[kBI], const i32x4 (&cb)[kBJ], i32x4 (&na)[kBI],
                      i32x4 (&nb)[kBJ], int rstage, int rks, int c) {
@@ -695,7 +689,7 @@ __device__ __forceinline__ void gemm_tile_chain_split(const Operand& A, const Op
   if (first) {
     issue(0);
     issue(1);
-    wait_vm<2 * kLoads>();   // stage 0 landed; stage 1 may be in flight
+    wait_vm<4 * kLoads>();   // stage 0 landed; stage 1 may be in flight
     pipe_barrier();
     const lds_t* s = lds;
 #pragma unroll
