@@ -706,14 +706,12 @@ __device__ __forceinline__ void gemm_tile_chain_mn(const Operand& A, const Opera
     for (int c = 0; c < 4; ++c) quarter(fa0, fb0, fa1, fb1, kt, 1, c);
     wait_vm<0>();
     pipe_barrier();
+    // (the burst goes out before the first quarter here: 0.13 ms faster for the
+    // gradient launch than after it, while the logit products lost by it)
+    issue(kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      quarter(fa1, fb1, fa0, fb0, kt + 1, 0, c);
-      if (c == 0) {
-        issue(kt + 2);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
+    for (int c = 0; c < 4; ++c) quarter(fa1, fb1, fa0, fb0, kt + 1, 0, c);
   }
   if (!has_next) {
     wait_vm<0>();
