@@ -539,7 +539,8 @@ __device__ __forceinline__ void gemm_tile_chain(const Operand& A, const Operand&
   const uint32_t offA1 = load_offset<T>(A, lw + kHalf, lane, stepA);
   const uint32_t offB0 = load_offset<T>(B, lw, lane, stepB);
   const uint32_t offB1 = load_offset<T>(B, lw + kHalf, lane, stepB);
-  auto issue = [&](int stage) {
+  // (which: 1 = A's loads, 2 = B's, 3 = both)
+  auto issue = [&](int stage, int which) {
     if (wave >= kHalf) return;
     const uint32_t s0 = lds_base + (stage & 1) * kStageLds + lw * 1024;
     const bool nxt = has_next && stage >= nk;
@@ -551,8 +552,8 @@ __device__ __forceinline__ void gemm_tile_chain(const Operand& A, const Operand&
     const __amdgpu_buffer_rsrc_t ra = range_rsrc(xa.base + o, xa.limit - o);
     const __amdgpu_buffer_rsrc_t rb = range_rsrc(xb.base + o, xb.limit - o);
     const uint32_t l = __builtin_amdgcn_readfirstlane(s0);
-    dma16_split(ra, offA0, offA1, __builtin_amdgcn_readfirstlane(stepA), l);
-    dma16_split(rb, offB0, offB1, __builtin_amdgcn_readfirstlane(stepB), l + kOpLds);
+    if (which & 1) dma16_split(ra, offA0, offA1, __builtin_amdgcn_readfirstlane(stepA), l);
+    if (which & 2) dma16_split(rb, offB0, offB1, __builtin_amdgcn_readfirstlane(stepB), l + kOpLds);
   };
   auto quarter = [&](const i32x4 (&ca)[kBI], const i32x4 (&cb)[kBJ], i32x4 (&na)[kBI],
                      i32x4 (&nb)[kBJ], int rstage, int rks, int c) {
@@ -577,8 +578,8 @@ __device__ __forceinline__ void gemm_tile_chain(const Operand& A, const Operand&
 
   i32x4 fa1[kBI], fb1[kBJ];
   if (first) {
-    issue(0);
-    issue(1);
+    issue(0, 3);
+    issue(1, 3);
     wait_vm<4 * kLoads>();   // stage 0 landed; stage 1 may be in flight
     pipe_barrier();
     const lds_t* s = lds;
@@ -596,8 +597,14 @@ __device__ __forceinline__ void gemm_tile_chain(const Operand& A, const Operand&
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       quarter(fa1, fb1, fa0, fb0, kt + 1, 0, c);
+      // stage kt + 2's loads: B's after quarter 0, A's after quarter 1 (one burst of
+      // both after quarter 0 ran the dlogits tiles 1.5% slower, the forward's 0.5%)
       if (c == 0) {
-        issue(kt + 2);
+        issue(kt + 2, 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c == 1) {
+        issue(kt + 2, 1);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -651,7 +658,8 @@ __device__ __forceinline__ void gemm_tile_chain_mn(const Operand& A, const Opera
   const uint32_t offB0 = load_offset<T, kBlockedB ? 1 : 0>(B, lw, lane, stepB);
   const uint32_t offB1 = load_offset<T, kBlockedB ? 1 : 0>(B, lw + kHalf, lane, stepB);
   const int64_t strideA = stage_stride<T>(A, false), strideB = stage_stride<T>(B, true);
-  auto issue = [&](int stage) {
+  // (which: 1 = A's loads, 2 = B's, 3 = both)
+  auto issue = [&](int stage, int which) {
     if (wave >= kHalf) return;
     const uint32_t s0 = lds_base + (stage & 1) * kStageLds + lw * 1024;
     const bool nxt = has_next && stage >= nk;
@@ -661,8 +669,8 @@ __device__ __forceinline__ void gemm_tile_chain_mn(const Operand& A, const Opera
     const __amdgpu_buffer_rsrc_t ra = range_rsrc(xa.base + oa, xa.limit - oa);
     const __amdgpu_buffer_rsrc_t rb = range_rsrc(xb.base + ob, xb.limit - ob);
     const uint32_t l = __builtin_amdgcn_readfirstlane(s0);
-    dma16_split(ra, offA0, offA1, __builtin_amdgcn_readfirstlane(stepA), l);
-    dma16_split(rb, offB0, offB1, __builtin_amdgcn_readfirstlane(stepB), l + kOpLds);
+    if (which & 1) dma16_split(ra, offA0, offA1, __builtin_amdgcn_readfirstlane(stepA), l);
+    if (which & 2) dma16_split(rb, offB0, offB1, __builtin_amdgcn_readfirstlane(stepB), l + kOpLds);
   };
   auto quarter = [&](const i32x4 (&ca)[kBI], const i32x4 (&cb)[kBJ], i32x4 (&na)[kBI],
                      i32x4 (&nb)[kBJ], int rstage, int rks, int c) {
@@ -687,8 +695,8 @@ __device__ __forceinline__ void gemm_tile_chain_mn(const Operand& A, const Opera
 
   i32x4 fa1[kBI], fb1[kBJ];
   if (first) {
-    issue(0);
-    issue(1);
+    issue(0, 3);
+    issue(1, 3);
     wait_vm<4 * kLoads>();   // stage 0 landed; stage 1 may be in flight
     pipe_barrier();
     const lds_t* s = lds;
@@ -706,12 +714,20 @@ __device__ __forceinline__ void gemm_tile_chain_mn(const Operand& A, const Opera
     for (int c = 0; c < 4; ++c) quarter(fa0, fb0, fa1, fb1, kt, 1, c);
     wait_vm<0>();
     pipe_barrier();
-    // (the burst goes out before the first quarter here: 0.13 ms faster for the
-    // gradient launch than after it, while the logit products lost by it)
-    issue(kt + 2);
+    // stage kt + 2's loads: B's right after the barrier, A's after quarter 1.  The
+    // gradient launch ran 2.3% slower with one burst of both right after the
+    // barrier, and that was 1.3% faster than one burst after quarter 0.  (The logit
+    // products lose with loads issued before quarter 0.)
+    issue(kt + 2, 2);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) quarter(fa1, fb1, fa0, fb0, kt + 1, 0, c);
+    for (int c = 0; c < 4; ++c) {
+      quarter(fa1, fb1, fa0, fb0, kt + 1, 0, c);
+      if (c == 1) {
+        issue(kt + 2, 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
   if (!has_next) {
     wait_vm<0>();
