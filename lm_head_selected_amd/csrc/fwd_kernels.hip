@@ -51,23 +51,24 @@ __device__ __forceinline__ void tile_partials(f32x4 (&acc)[kBI][kBJ], const FwdT
 #pragma unroll
     for (int i = 0; i < kBI; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[i][j][e] *= c2;          // padded rows stay -inf (c2 > 0)
-        m = fmaxf(m, acc[i][j][e]);
-      }
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, acc[i][j][e]);
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
+    // the maximum of the raw logits, scaled once: scaling by c2 > 0 keeps the order,
+    // so this is the maximum of the scaled logits, and each exponent argument is one
+    // fma (z * c2 - m2) rather than a multiply and a subtraction
+    const float m2 = m * c2;
     float s = 0.0f;
     if (m != -INFINITY) {
 #pragma unroll
       for (int i = 0; i < kBI; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s += fast_exp2(acc[i][j][e] - m);
+        for (int e = 0; e < 4; ++e) s += fast_exp2(__builtin_fmaf(acc[i][j][e], c2, -m2));
     }
     s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
     // all four lane groups hold the same (m, s); all write it
-    half_stats[wm][tl] = make_float2(m, s);
+    half_stats[wm][tl] = make_float2(m2, s);
   }
   if (kChained) pipe_barrier();
   else __syncthreads();
